@@ -1,0 +1,100 @@
+"""Oracle of the host bitwidth planner.
+
+The quality-aware planner lowers the precision of the least sensitive experts
+first, keeps key experts at full precision, never goes below an expert's
+bitwidth floor, and only moves to more aggressive plans as memory pressure
+rises ("内存的饥饿游戏", zhichai.net, sections "核心洞察：权重也能分页" and
+"安全边界与异步搬运").  The second summary states the budget M_w = M_total -
+M_kv, the integer program max sum_i I_i Q_i s.t. sum_i S(Q_i) <= M_w, and a
+greedy approximation that keeps important experts at high precision until the
+memory runs out ("动态量化优化MoE模型服务", time-frame.cloud, section
+"方法与技术路线").
+
+Reading taken here, which satisfies both descriptions: a demotion sequence.
+Start every expert at its highest level; while the plan is over budget, lower
+by one level the expert (not yet at its floor) whose next step costs the least
+harm per byte saved, ties to the larger saving, then the lower index.  The
+sequence does not depend on the budget, so plans are nested across budgets.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+OK = 0
+ENOSPACE = -3
+EINVAL = -1
+
+
+def plan_bitwidths(levels, harm, nbytes, floor_bits, budget):
+    """Return (status, bits[E]) for the demotion-sequence greedy.
+
+    levels      bitwidths from high to low, e.g. [16, 6, 5, 4, 3]
+    harm        [E][L] quality loss of running expert e at level l (>= 0)
+    nbytes      [E][L] bytes of expert e at level l (strictly decreasing in l)
+    floor_bits  [E] lowest bitwidth allowed per expert (must be one of levels)
+    budget      bytes available to expert weights
+    """
+    levels = [int(v) for v in levels]
+    E = len(floor_bits)
+    L = len(levels)
+    harm = [[float(harm[e][l]) for l in range(L)] for e in range(E)]
+    nb = [[int(nbytes[e][l]) for l in range(L)] for e in range(E)]
+    floor_lvl = []
+    for e in range(E):
+        if int(floor_bits[e]) not in levels:
+            return EINVAL, None
+        floor_lvl.append(levels.index(int(floor_bits[e])))
+    for e in range(E):
+        for l in range(L - 1):
+            if not nb[e][l] > nb[e][l + 1]:
+                return EINVAL, None
+
+    lvl = [0] * E
+    total = sum(nb[e][0] for e in range(E))
+    while total > budget:
+        best = None
+        for e in range(E):
+            l = lvl[e]
+            if l >= floor_lvl[e]:
+                continue
+            saved = nb[e][l] - nb[e][l + 1]
+            cost = (harm[e][l + 1] - harm[e][l]) / float(saved)
+            key = (cost, -saved, e)
+            if best is None or key < best[0]:
+                best = (key, e)
+        if best is None:
+            return ENOSPACE, np.array([levels[floor_lvl[e]] for e in range(E)], dtype=np.int8)
+        e = best[1]
+        total -= nb[e][lvl[e]] - nb[e][lvl[e] + 1]
+        lvl[e] += 1
+    return OK, np.array([levels[lvl[e]] for e in range(E)], dtype=np.int8)
+
+
+def plan_total(levels, nbytes, bits):
+    levels = [int(v) for v in levels]
+    return sum(int(nbytes[e][levels.index(int(b))]) for e, b in enumerate(bits))
+
+
+def plan_harm(levels, harm, bits):
+    levels = [int(v) for v in levels]
+    return sum(float(harm[e][levels.index(int(b))]) for e, b in enumerate(bits))
+
+
+def brute_force(levels, harm, nbytes, floor_bits, budget):
+    """Exact minimum-harm plan within the budget by enumeration (tiny E only)."""
+    levels = [int(v) for v in levels]
+    E = len(floor_bits)
+    choices = [range(0, levels.index(int(floor_bits[e])) + 1) for e in range(E)]
+    best = None
+    for assign in itertools.product(*choices):
+        tot = sum(int(nbytes[e][l]) for e, l in enumerate(assign))
+        if tot > budget:
+            continue
+        h = sum(float(harm[e][l]) for e, l in enumerate(assign))
+        if best is None or h < best[0]:
+            best = (h, assign)
+    if best is None:
+        return None, None
+    return best[0], np.array([levels[l] for l in best[1]], dtype=np.int8)
