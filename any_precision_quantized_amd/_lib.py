@@ -1,0 +1,198 @@
+"""ctypes binding of libapmoe.so (C ABI in include/apmoe.h).
+
+Argument marshalling only: every function here checks dtypes, devices and
+sizes of torch tensors on the host, takes their device pointers and the
+current HIP stream, and calls the entry point of the same name.  All compute
+runs in the library's HIP kernels.  There is no fallback: a missing or
+unloadable library raises ApmoeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libapmoe.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "apmoe.h")
+
+OK, EINVAL, EBITS, ENOSPACE, EHIP = 0, -1, -2, -3, -4
+GATE_UP_SWIGLU, DOWN = 0, 1
+ONLY_GEMV, ONLY_TILE = 0x10, 0x20
+MAX_EXPERTS = 256
+
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+
+class ApmoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib().apmoe_strerror(code).decode() if code < 0 else "library not available"
+        super().__init__(f"{where}: {msg} ({code})")
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m any_precision_quantized_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "apmoe_route": [_vp, _c_int, _c_int, _vp, _vp, ctypes.c_float, _c_int, _c_int, _vp, _vp, _vp],
+            "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp],
+            "apmoe_bitplane_lut_gemm": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
+                                        _c_int, _c_int, _c_int, _vp, _c_size, _vp],
+            "apmoe_combine": [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp],
+            "apmoe_plan_bitwidths": [_c_int, _c_int, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp],
+            "apmoe_commit_bits": [_vp, _c_int, _vp, _vp],
+            "apmoe_workspace_bytes": [_c_int, _c_int, _c_int, _c_int, _c_int],
+            "apmoe_strerror": [_c_int],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = _c_int
+        lib.apmoe_workspace_bytes.restype = _c_size
+        lib.apmoe_strerror.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def header_symbols():
+    """Entry points declared in include/apmoe.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(apmoe_\w+)\s*\(", text, re.M)))
+
+
+def strerror(code: int) -> str:
+    return _lib().apmoe_strerror(int(code)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != OK:
+        raise ApmoeError(rc, where)
+
+
+# ---------------------------------------------------------------------------
+# torch helpers (device memory and streams only)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtype=None, numel=None, name="tensor", device=True):
+    if t is None:
+        return None
+    torch = _torch()
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if device and t.device.type != "cuda":
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI, without the prefix)
+# ---------------------------------------------------------------------------
+
+def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, stream=None):
+    torch = _torch()
+    T, H = x.shape
+    E = w_router.shape[0]
+    rc = _lib().apmoe_route(_ptr(x, torch.float16, T * H, "x"), T, H,
+                            _ptr(w_router, torch.float32, E * H, "w_router"),
+                            _ptr(bias, torch.float32, E, "bias"), float(logit_scale), E, k,
+                            _ptr(topk_ids, torch.int32, T * k, "topk_ids"),
+                            _ptr(topk_w, torch.float32, T * k, "topk_w"), _stream(stream))
+    _check(rc, "apmoe_route")
+
+
+def permute(topk_ids, E, counts, offsets, sorted_slots, pos_of_slot, stream=None):
+    torch = _torch()
+    T, k = topk_ids.shape
+    S = T * k
+    rc = _lib().apmoe_permute(_ptr(topk_ids, torch.int32, S, "topk_ids"), T, k, E,
+                              _ptr(counts, torch.int32, E, "counts"),
+                              _ptr(offsets, torch.int32, E + 1, "offsets"),
+                              _ptr(sorted_slots, torch.int32, S, "sorted_slots"),
+                              _ptr(pos_of_slot, torch.int32, S, "pos_of_slot"), None, 0,
+                              _stream(stream))
+    _check(rc, "apmoe_permute")
+
+
+def workspace_bytes(T, k, E, H, I) -> int:
+    return int(_lib().apmoe_workspace_bytes(T, k, E, H, I))
+
+
+def bitplane_lut_gemm(stage, experts_desc, bits, E, offsets, sorted_slots, k, inp, out, T, H, I,
+                      mfma_min_tokens, ws=None, stream=None):
+    """experts_desc: device tensor holding E apmoe_expert descriptors (see ExpertTable)."""
+    torch = _torch()
+    S = T * k
+    base = stage & ~(ONLY_GEMV | ONLY_TILE)
+    if base == GATE_UP_SWIGLU:
+        _ptr(inp, torch.float16, T * H, "x")
+        _ptr(out, torch.float16, S * I, "A")
+    elif base == DOWN:
+        _ptr(inp, torch.float16, S * I, "A")
+        _ptr(out, torch.float32, S * H, "Y")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = _lib().apmoe_bitplane_lut_gemm(
+        int(stage), _ptr(experts_desc, torch.int64, E * 18, "experts"), _ptr(bits, torch.int8, E, "bits"), E,
+        _ptr(offsets, torch.int32, E + 1, "offsets"), _ptr(sorted_slots, torch.int32, None, "sorted_slots"),
+        k, inp.data_ptr(), out.data_ptr(), T, H, I, int(mfma_min_tokens),
+        None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
+    _check(rc, "apmoe_bitplane_lut_gemm")
+
+
+def combine(Y, pos_of_slot, topk_w, T, k, H, y_shared, out, stream=None):
+    torch = _torch()
+    rc = _lib().apmoe_combine(_ptr(Y, torch.float32, T * k * H, "Y"),
+                              _ptr(pos_of_slot, torch.int32, T * k, "pos_of_slot"),
+                              _ptr(topk_w, torch.float32, T * k, "topk_w"), T, k, H,
+                              _ptr(y_shared, torch.float32, T * H, "y_shared"),
+                              _ptr(out, torch.float16, T * H, "out"), _stream(stream))
+    _check(rc, "apmoe_combine")
+
+
+def commit_bits(bits_host, bits_dev, stream=None):
+    """bits_host: a sequence of ints; bits_dev: device int8 tensor [E]."""
+    import numpy as np
+    torch = _torch()
+    b = np.ascontiguousarray(np.asarray(bits_host, dtype=np.int8))
+    rc = _lib().apmoe_commit_bits(b.ctypes.data, len(b), _ptr(bits_dev, torch.int8, len(b), "bits_dev"),
+                                  _stream(stream))
+    _check(rc, "apmoe_commit_bits")
+
+
+def plan_bitwidths(levels, harm, nbytes, floor_bits, budget):
+    """Host planner.  Returns (status, bits int8[E]); raises only on EINVAL/EBITS."""
+    import numpy as np
+    lv = np.ascontiguousarray(np.asarray(levels, dtype=np.int8))
+    hm = np.ascontiguousarray(np.asarray(harm, dtype=np.float64))
+    nb = np.ascontiguousarray(np.asarray(nbytes, dtype=np.uint64))
+    fl = np.ascontiguousarray(np.asarray(floor_bits, dtype=np.int8))
+    E, L = hm.shape
+    if nb.shape != (E, L) or lv.shape != (L,) or fl.shape != (E,):
+        raise ValueError("planner input shapes disagree")
+    out = np.zeros(E, dtype=np.int8)
+    rc = _lib().apmoe_plan_bitwidths(E, L, lv.ctypes.data, hm.ctypes.data, nb.ctypes.data,
+                                     fl.ctypes.data, int(budget), out.ctypes.data)
+    return rc, out

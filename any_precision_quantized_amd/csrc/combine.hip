@@ -1,0 +1,81 @@
+// Weighted scatter-combine, the bitwidth-table commit and the small host entry points.
+#include "common.hpp"
+
+namespace apmoe {
+
+// out[t][h] = sum_j w[t][j] * Y[pos[t*k+j]][h] (+ y_shared[t][h]), fp32 in
+// ascending j, one rounding to fp16.  One thread per 4 consecutive h.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
+                                                      const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ w, int T, int k,
+                                                      int H, const float* __restrict__ ysh,
+                                                      half_t* __restrict__ out) {
+    const int t = blockIdx.y;
+    const int h = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (t >= T || h >= H) return;
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const float g = w[(size_t)t * k + j];
+        const float4_t y = *reinterpret_cast<const float4_t*>(Y + (size_t)pos[(size_t)t * k + j] * H + h);
+        acc = acc + g * y;
+    }
+    if (ysh) acc = acc + *reinterpret_cast<const float4_t*>(ysh + (size_t)t * H + h);
+    half4_t o = {(half_t)acc[0], (half_t)acc[1], (half_t)acc[2], (half_t)acc[3]};
+    *reinterpret_cast<half4_t*>(out + (size_t)t * H + h) = o;
+}
+
+struct BitsArg {
+    int8_t v[APMOE_MAX_EXPERTS];
+};
+
+__global__ void commit_bits_kernel(BitsArg bits, int E, int8_t* __restrict__ dst) {
+    const int e = threadIdx.x;
+    if (e < E) dst[e] = bits.v[e];
+}
+
+}  // namespace apmoe
+
+using namespace apmoe;
+
+extern "C" int apmoe_combine(const float* Y, const int32_t* pos_of_slot, const float* topk_w, int T,
+                             int k, int H, const float* y_shared, uint16_t* out, void* stream) {
+    if (T < 0 || k < 1 || H <= 0 || H % 32) return APMOE_EINVAL;
+    if (T == 0) return APMOE_OK;
+    if (!Y || !pos_of_slot || !topk_w || !out) return APMOE_EINVAL;
+    dim3 grid((H / 4 + 255) / 256, T);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, as_stream(stream), Y, pos_of_slot, topk_w,
+                       T, k, H, y_shared, reinterpret_cast<half_t*>(out));
+    return launch_status();
+}
+
+extern "C" int apmoe_commit_bits(const int8_t* bits_host, int E, int8_t* bits_dev, void* stream) {
+    if (E < 1 || E > APMOE_MAX_EXPERTS || !bits_host || !bits_dev) return APMOE_EINVAL;
+    BitsArg a = {};
+    for (int e = 0; e < E; ++e) {
+        if (!valid_bits(bits_host[e])) return APMOE_EBITS;
+        a.v[e] = bits_host[e];
+    }
+    hipLaunchKernelGGL(commit_bits_kernel, dim3(1), dim3(APMOE_MAX_EXPERTS), 0, as_stream(stream), a,
+                       E, bits_dev);
+    return launch_status();
+}
+
+extern "C" size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I) {
+    (void)T;
+    (void)k;
+    (void)E;
+    (void)H;
+    (void)I;
+    return 0;
+}
+
+extern "C" const char* apmoe_strerror(int code) {
+    switch (code) {
+        case APMOE_OK: return "ok";
+        case APMOE_EINVAL: return "invalid argument (shape, pointer or stage)";
+        case APMOE_EBITS: return "bitwidth outside {3,4,5,6,16}";
+        case APMOE_ENOSPACE: return "workspace too small or budget infeasible";
+        case APMOE_EHIP: return "HIP runtime error at launch";
+        default: return "unknown error";
+    }
+}

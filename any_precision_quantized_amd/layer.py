@@ -1,0 +1,166 @@
+"""Device-resident expert weights and the layer's call sequence.
+
+``ExpertTable`` uploads per-expert bit-planes, LUTs and fp16 rows and builds
+the device array of ``apmoe_expert`` descriptors.  ``MoELayer`` owns the
+per-call buffers and chains the C-ABI entry points:
+
+    route -> permute -> gemm(GATE_UP_SWIGLU) -> gemm(DOWN) [-> shared expert] -> combine
+
+PyTorch only provides device memory and the HIP stream; every step runs in
+libapmoe's kernels.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+
+from . import _lib
+
+MATS = ("gate", "up", "down")
+DESC_WORDS = 18          # 3 matrices x (planes, lut[4], w16) pointers
+# Groups of at least this many slots take the dequantise-to-LDS + MFMA tile path.
+DEFAULT_MFMA_MIN_TOKENS = 16
+
+
+class ExpertTable:
+    """Expert weights in device memory plus their descriptor array.
+
+    ``experts``: sequence of mappings name -> matrix, each matrix exposing
+    ``planes`` (uint32 [6, rows, cols/32]), ``luts`` (four fp16 arrays
+    [rows, 2**b]) and ``w16`` (fp16 [rows, cols] or None).
+    """
+
+    def __init__(self, experts, device="cuda", _tensors=None):
+        import torch
+        self.device = device
+        self.E = len(experts) if experts is not None else len(_tensors)
+        self.tensors: List[dict] = []
+        if _tensors is None:
+            for mats in experts:
+                d = {}
+                for name in MATS:
+                    m = mats[name]
+                    ent = {"planes": None, "luts": [None] * 4, "w16": None}
+                    if m.planes is not None and m.planes.size:
+                        ent["planes"] = torch.from_numpy(np.ascontiguousarray(m.planes).view(np.int32)).to(device)
+                    for i, lut in enumerate(m.luts or []):
+                        ent["luts"][i] = torch.from_numpy(np.ascontiguousarray(lut).view(np.int16)).to(device)
+                    if m.w16 is not None:
+                        ent["w16"] = torch.from_numpy(np.ascontiguousarray(m.w16).view(np.int16)).to(device)
+                    d[name] = ent
+                self.tensors.append(d)
+        else:
+            self.tensors = _tensors
+        self.desc = self._descriptors()
+
+    def _descriptors(self):
+        import torch
+        desc = np.zeros((self.E, DESC_WORDS), dtype=np.int64)
+        for e, d in enumerate(self.tensors):
+            for mi, name in enumerate(MATS):
+                ent = d[name]
+                base = 6 * mi
+                if ent["planes"] is not None:
+                    desc[e, base] = ent["planes"].data_ptr()
+                for i in range(4):
+                    if ent["luts"][i] is not None:
+                        desc[e, base + 1 + i] = ent["luts"][i].data_ptr()
+                if ent["w16"] is not None:
+                    desc[e, base + 5] = ent["w16"].data_ptr()
+        return torch.from_numpy(desc).to(self.device)
+
+    def replicate(self) -> "ExpertTable":
+        """A second copy of every weight tensor (device-side clone)."""
+        copies = []
+        for d in self.tensors:
+            copies.append({name: {"planes": None if ent["planes"] is None else ent["planes"].clone(),
+                                  "luts": [None if t is None else t.clone() for t in ent["luts"]],
+                                  "w16": None if ent["w16"] is None else ent["w16"].clone()}
+                           for name, ent in d.items()})
+        return ExpertTable(None, self.device, _tensors=copies)
+
+    def nbytes(self) -> int:
+        n = 0
+        for d in self.tensors:
+            for ent in d.values():
+                for t in [ent["planes"], ent["w16"], *ent["luts"]]:
+                    if t is not None:
+                        n += t.numel() * t.element_size()
+        return n
+
+
+class MoELayer:
+    """One MoE expert-FFN layer call on the GPU through libapmoe."""
+
+    def __init__(self, E, H, I, k, T, w_router, bias, logit_scale, experts: ExpertTable, bits,
+                 shared: Optional[ExpertTable] = None, shared_I: int = 0, mfma_min_tokens: int = DEFAULT_MFMA_MIN_TOKENS,
+                 device="cuda"):
+        import torch
+        self.E, self.H, self.I, self.k, self.T = E, H, I, k, T
+        self.logit_scale = float(logit_scale)
+        self.mfma_min_tokens = int(mfma_min_tokens)
+        self.device = device
+        dev = dict(device=device)
+        self.w_router = torch.as_tensor(np.ascontiguousarray(w_router), dtype=torch.float32).to(device)
+        self.bias = None if bias is None else torch.as_tensor(np.ascontiguousarray(bias), dtype=torch.float32).to(device)
+        self.experts = experts
+        self.bits = torch.zeros(E, dtype=torch.int8, **dev)
+        self.commit(bits)
+        S = T * k
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, **dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, **dev)
+        self.counts = torch.empty(E, dtype=torch.int32, **dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, **dev)
+        self.sorted_slots = torch.empty(S, dtype=torch.int32, **dev)
+        self.pos_of_slot = torch.empty(S, dtype=torch.int32, **dev)
+        self.A = torch.empty((S, I), dtype=torch.float16, **dev)
+        self.Y = torch.empty((S, H), dtype=torch.float32, **dev)
+        self.out = torch.empty((T, H), dtype=torch.float16, **dev)
+        nws = _lib.workspace_bytes(T, k, E, H, max(I, shared_I or 0))
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, **dev) if nws else None
+        self.shared = shared
+        self.shared_I = shared_I
+        if shared is not None:
+            self.sh_bits = torch.tensor([16], dtype=torch.int8, **dev)
+            self.sh_offsets = torch.tensor([0, T], dtype=torch.int32, **dev)
+            self.sh_slots = torch.arange(T, dtype=torch.int32, **dev)
+            self.A_sh = torch.empty((T, shared_I), dtype=torch.float16, **dev)
+            self.Y_sh = torch.empty((T, H), dtype=torch.float32, **dev)
+
+    def commit(self, bits):
+        _lib.commit_bits(bits, self.bits)
+
+    def forward(self, x, experts: Optional[ExpertTable] = None, shared: Optional[ExpertTable] = None):
+        """x: device fp16 [T, H].  Returns the fp16 output [T, H] (a buffer reused by later calls)."""
+        ex = self.experts if experts is None else experts
+        sh = self.shared if shared is None else shared
+        T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
+        _lib.route(x, self.w_router, self.bias, self.logit_scale, k, self.topk_ids, self.topk_w)
+        _lib.permute(self.topk_ids, E, self.counts, self.offsets, self.sorted_slots, self.pos_of_slot)
+        _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, ex.desc, self.bits, E, self.offsets, self.sorted_slots,
+                               k, x, self.A, T, H, I, self.mfma_min_tokens, self.ws)
+        _lib.bitplane_lut_gemm(_lib.DOWN, ex.desc, self.bits, E, self.offsets, self.sorted_slots,
+                               k, self.A, self.Y, T, H, I, self.mfma_min_tokens, self.ws)
+        ysh = None
+        if sh is not None:
+            _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, sh.desc, self.sh_bits, 1, self.sh_offsets,
+                                   self.sh_slots, 1, x, self.A_sh, T, H, self.shared_I,
+                                   self.mfma_min_tokens, self.ws)
+            _lib.bitplane_lut_gemm(_lib.DOWN, sh.desc, self.sh_bits, 1, self.sh_offsets, self.sh_slots,
+                                   1, self.A_sh, self.Y_sh, T, H, self.shared_I, self.mfma_min_tokens,
+                                   self.ws)
+            ysh = self.Y_sh
+        _lib.combine(self.Y, self.pos_of_slot, self.topk_w, T, k, H, ysh, self.out)
+        return self.out
+
+
+def from_inputs(inp, bits=None, mfma_min_tokens=DEFAULT_MFMA_MIN_TOKENS, device="cuda"):
+    """Build device weights and a layer from a generated input set (duck-typed)."""
+    cfg = inp.cfg
+    experts = ExpertTable(inp.experts, device)
+    shared = ExpertTable([inp.shared], device) if inp.shared is not None else None
+    b = inp.bits if bits is None else bits
+    layer = MoELayer(cfg.E, cfg.H, cfg.I, cfg.k, cfg.T, inp.w_router, inp.bias, cfg.logit_scale, experts,
+                     b, shared, cfg.shared_I, mfma_min_tokens, device)
+    return layer

@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of one any-precision MoE-layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen_decode]
+
+A step is the whole layer on one batch: route -> permute -> gate/up+SwiGLU ->
+down (each on the bit-plane GEMV path and/or the MFMA tile path) -> the fp16
+shared expert where the layer has one -> weighted combine.  Inputs are
+synthetic and already resident in HBM; the expert weights rotate over R
+device replicas so every step reads its planes from HBM rather than from the
+256 MB MALL.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+FP16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+METRIC = "MoE-layer tokens/s + effective HBM GB/s (% of peak) at mixed 3–6 bit experts"
+
+
+def expert_bytes(H, I, b):
+    """Algorithmic weight bytes of gate+up and of down at bitwidth b."""
+    if b == 16:
+        return 2 * I * H * 2, H * I * 2
+    return 2 * (I * H * b // 8 + I * (1 << b) * 2), H * I * b // 8 + H * (1 << b) * 2
+
+
+def algorithmic(cfg, bits, counts, mfma_min):
+    """Bytes each launch must move (planes of the top b bits + LUT_b, or fp16 rows,
+    plus activations in and out) and the expert flops."""
+    H, I, T, k, E = cfg.H, cfg.I, cfg.T, cfg.k, cfg.E
+    by = {"route": T * H * 2 + E * H * 4 + (E * 4 if cfg.router_bias else 0) + T * k * 8,
+          "permute": T * k * 4 + (2 * E + 1) * 4 + T * k * 8,
+          "gate_up_gemv": 0, "gate_up_tile": 0, "down_gemv": 0, "down_tile": 0,
+          "shared_gate_up": 0, "shared_down": 0,
+          "combine": T * k * (H * 4 + 8) + T * H * 2 + (T * H * 4 if cfg.shared_I else 0)}
+    flops = 0
+    for e in range(E):
+        m = int(counts[e])
+        if m == 0:
+            continue
+        wgu, wd = expert_bytes(H, I, int(bits[e]))
+        path = "tile" if m >= mfma_min else "gemv"
+        by["gate_up_" + path] += wgu + m * H * 2 + m * I * 2
+        by["down_" + path] += wd + m * I * 2 + m * H * 4
+        flops += 6 * m * H * I
+    if cfg.shared_I:
+        Is = cfg.shared_I
+        by["shared_gate_up"] = 2 * Is * H * 2 + T * H * 2 + T * Is * 2
+        by["shared_down"] = H * Is * 2 + T * Is * 2 + T * H * 4
+        flops += 6 * T * H * Is
+    return by, flops
+
+
+def cpu_baseline(inp, bits):
+    """The float64 oracle on the host cores, one full step of the same workload."""
+    from threadpoolctl import threadpool_info
+    from oracle import moe
+    t0 = time.perf_counter()
+    moe.layer(inp, bits=bits)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": inp.cfg.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full layer step ({inp.cfg.T} tokens) of the same workload in float64 NumPy, "
+                      f"{dt:.1f} s; BLAS threads {threads} of {len(os.sched_getaffinity(0))} host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen_decode")
+    ap.add_argument("--mfma-min-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replica-bytes", type=float, default=1.0e9,
+                    help="weight bytes the rotating replicas must span (MALL defeat)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this layer runs on one GPU; --gpus must be 1 (no multi-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from any_precision_quantized_amd import _lib
+    from any_precision_quantized_amd import layer as L
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cfg = synth.get(args.workload)
+    mfma_min = args.mfma_min_tokens or L.DEFAULT_MFMA_MIN_TOKENS
+    inp = synth.make_inputs(cfg, seed=0)
+    if inp.bits is None:
+        pl = inp.plan
+        st, bits = _lib.plan_bitwidths(pl["levels"], pl["harm"], pl["bytes"], pl["floors"], pl["budget"])
+        if st != _lib.OK:
+            raise RuntimeError(f"planner: {_lib.strerror(st)}")
+    else:
+        bits = np.asarray(inp.bits, dtype=np.int8)
+
+    layer = L.from_inputs(inp, bits=bits, mfma_min_tokens=mfma_min)
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
+    layer.forward(x)
+    torch.cuda.synchronize()
+    counts = layer.counts.cpu().numpy()
+    by, flops = algorithmic(cfg, bits, counts, mfma_min)
+    step_bytes = sum(by.values())
+    weight_bytes = sum(v for k_, v in by.items() if k_.startswith(("gate_up", "down", "shared")))
+    R = max(2, math.ceil(args.replica_bytes / max(1, weight_bytes)))
+    tables = [layer.experts] + [layer.experts.replicate() for _ in range(R - 1)]
+    shared = [layer.shared] + ([layer.shared.replicate() for _ in range(R - 1)] if layer.shared else [None] * (R - 1))
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    lib = _lib._lib()
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    ws, wsb = (p(layer.ws), layer.ws.numel()) if layer.ws is not None else (None, 0)
+
+    # Every launch of a step as (name, callable) with its raw arguments bound once.
+    def launches(r):
+        tab, sh = tables[r], shared[r]
+        seq = [
+            ("route", lambda: lib.apmoe_route(p(x), T, H, p(layer.w_router), p(layer.bias), layer.logit_scale,
+                                              E, k, p(layer.topk_ids), p(layer.topk_w), sp)),
+            ("permute", lambda: lib.apmoe_permute(p(layer.topk_ids), T, k, E, p(layer.counts), p(layer.offsets),
+                                                  p(layer.sorted_slots), p(layer.pos_of_slot), None, 0, sp)),
+        ]
+        for stage, name, src, dst in ((_lib.GATE_UP_SWIGLU, "gate_up", x, layer.A),
+                                      (_lib.DOWN, "down", layer.A, layer.Y)):
+            for flag, path in ((_lib.ONLY_GEMV, "gemv"), (_lib.ONLY_TILE, "tile")):
+                seq.append((f"{name}_{path}", (lambda st=stage | flag, s_=src, d_=dst: lib.apmoe_bitplane_lut_gemm(
+                    st, p(tab.desc), p(layer.bits), E, p(layer.offsets), p(layer.sorted_slots), k, p(s_), p(d_),
+                    T, H, I, mfma_min, ws, wsb, sp))))
+        if sh is not None:
+            Is = cfg.shared_I
+            seq.append(("shared_gate_up", lambda: lib.apmoe_bitplane_lut_gemm(
+                _lib.GATE_UP_SWIGLU, p(sh.desc), p(layer.sh_bits), 1, p(layer.sh_offsets), p(layer.sh_slots), 1,
+                p(x), p(layer.A_sh), T, H, Is, mfma_min, ws, wsb, sp)))
+            seq.append(("shared_down", lambda: lib.apmoe_bitplane_lut_gemm(
+                _lib.DOWN, p(sh.desc), p(layer.sh_bits), 1, p(layer.sh_offsets), p(layer.sh_slots), 1,
+                p(layer.A_sh), p(layer.Y_sh), T, H, Is, mfma_min, ws, wsb, sp)))
+        ysh = p(layer.Y_sh) if sh is not None else None
+        seq.append(("combine", lambda: lib.apmoe_combine(p(layer.Y), p(layer.pos_of_slot), p(layer.topk_w), T, k,
+                                                          H, ysh, p(layer.out), sp)))
+        return seq
+
+    steps = [launches(r) for r in range(R)]
+    names = [n for n, _ in steps[0]]
+
+    def run(seq, timed_name=None, ev=None):
+        for n, fn in seq:
+            if n == timed_name:
+                ev[0].record(stream)
+                rc = fn()
+                ev[1].record(stream)
+            else:
+                rc = fn()
+            if rc != 0:
+                raise _lib.ApmoeError(rc, n)
+
+    # Per-launch durations (separate pass) to find the dominant kernel.
+    per = {n: 0.0 for n in names}
+    probe_steps = max(5, min(50, args.steps))
+    for i in range(args.warmup):
+        run(steps[i % R])
+    torch.cuda.synchronize()
+    for name in names:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(probe_steps)]
+        for i in range(probe_steps):
+            run(steps[i % R], name, evs[i])
+        torch.cuda.synchronize()
+        per[name] = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3   # us
+    dominant = max(names, key=lambda n: per[n])
+
+    # Timed region: K whole steps; the dominant launch is bracketed by events.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        run(steps[i % R])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(steps[i % R], dominant, evs[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dom_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
+
+    ms_per_step = dt / args.steps * 1e3
+    tokens_per_s = T * args.steps / dt
+    layer_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dom_bytes = by.get(dominant, 0)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: E{E} H{H} I{I} top-{k} T{T}"
+                               + (f" + fp16 shared expert I{cfg.shared_I}" if cfg.shared_I else "")
+                               + f", bits {dict(sorted((int(b), int((bits == b).sum())) for b in set(bits.tolist())))}",
+                   "mfma_min_tokens": mfma_min, "weight_replicas": R,
+                   "groups": sorted([int(c) for c in counts if c > 0], reverse=True)},
+        "hbm_gbs": layer_gbs,
+        "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+        "expert_tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": dom_bytes, "avg_us": dom_us},
+        "per_launch_us": {n: round(per[n], 2) for n in names},
+        "per_launch_bytes": {n: int(by.get(n, 0)) for n in names},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, bits)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

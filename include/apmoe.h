@@ -1,0 +1,171 @@
+/*
+ * apmoe.h - C ABI of libapmoe, an MI355X (gfx950) MoE expert-FFN layer over
+ * any-precision (bit-plane + LUT) expert weights.
+ *
+ * Method: each expert's weights are stored once as bit-planes plus per-row
+ * lookup tables and can be served at 3, 4, 5 or 6 bits or in an fp16
+ * fallback, switched at run time per expert ("内存的饥饿游戏：当 MoE 权重与
+ * KV 缓存争夺 GPU 的每一字节", zhichai.net, section "核心洞察：权重也能分页").
+ * A quality-aware planner picks the bitwidths under a memory budget (same
+ * page, sections "三层感知" and "安全边界与异步搬运"; "动态量化优化MoE模型服务",
+ * time-frame.cloud, section "方法与技术路线") and the new plan takes effect at
+ * a safe boundary between layer calls.
+ *
+ * Conventions (every entry point):
+ *  - Returns 0 (APMOE_OK) or a negative APMOE_E* code; apmoe_strerror names it.
+ *    Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is launched and no output is touched.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronises; all GPU work is enqueued on `stream` (a hipStream_t; NULL
+ *    means the default stream) in call order.  No global mutable state: calls
+ *    on different streams may run concurrently if their buffers are disjoint.
+ *  - Pointers are device pointers unless marked [host].  fp16 values travel
+ *    as uint16_t bit patterns (IEEE binary16).
+ *  - T = 0 is a successful no-op.
+ *
+ * Shapes: T tokens, E experts, H hidden, I expert intermediate, k top-k,
+ * slots S = T*k, slot s = t*k + j.  H and I must be multiples of 32.
+ */
+#ifndef APMOE_H
+#define APMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define APMOE_OK        0
+#define APMOE_EINVAL   (-1)   /* bad shape, null required pointer, bad stage */
+#define APMOE_EBITS    (-2)   /* a bitwidth outside {3,4,5,6,16} */
+#define APMOE_ENOSPACE (-3)   /* workspace too small, or planner budget infeasible */
+#define APMOE_EHIP     (-4)   /* the HIP runtime reported an error at launch */
+
+#define APMOE_GATE_UP_SWIGLU 0
+#define APMOE_DOWN           1
+/* Optional flags or-ed into `stage`: launch only one of the two paths
+ * (e.g. to run them on two streams, or to time them apart).  Neither flag
+ * (the default) launches both. */
+#define APMOE_ONLY_GEMV   0x10
+#define APMOE_ONLY_TILE   0x20
+
+#define APMOE_MAX_EXPERTS 256
+
+/*
+ * One weight matrix W [rows x cols], cols = the contraction dimension K.
+ *  planes : uint32 [6][rows][cols/32]; plane 0 holds the most significant bit
+ *           of each weight's 6-bit code; bit i of word w is column 32*w + i.
+ *           A b-bit expert reads only planes 0..b-1 (its code is the top b
+ *           bits of the 6-bit code).  Plane-major, so each plane is one slab.
+ *  lut[b-3]: fp16 [rows][1 << b], the b-bit centroid table of every row.
+ *  w16    : fp16 [rows][cols] plain weights, read only when the expert runs
+ *           at bitwidth 16; may be NULL for experts that never do.
+ * All pointers are device pointers; planes and lut may be NULL for an expert
+ * that only ever runs at 16 bits.
+ */
+typedef struct apmoe_mat {
+    const uint32_t* planes;
+    const uint16_t* lut[4];
+    const uint16_t* w16;
+} apmoe_mat;
+
+/* gate and up are [I x H]; down is [H x I]. */
+typedef struct apmoe_expert {
+    apmoe_mat gate, up, down;
+} apmoe_expert;
+
+/*
+ * Router: logits[t][e] = scale * (sum_h x[t][h] * w_router[e][h] + bias[e]),
+ * products and sums in float64; the top k experts by logit (ties to the lower
+ * index), listed by descending logit; gates = softmax over the k chosen logits.
+ *  x        fp16 [T][H]          w_router fp32 [E][H]
+ *  bias     fp32 [E] or NULL     logit_scale > 0
+ *  topk_ids int32 [T][k] (out)   topk_w   fp32 [T][k] (out)
+ * Needs 1 <= k <= E <= APMOE_MAX_EXPERTS, H > 0.
+ */
+int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const float* bias,
+                float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * Group slots by expert (stable: within an expert, slots in ascending order).
+ *  counts[e]       number of slots routed to e                    int32 [E]
+ *  offsets[e]      exclusive prefix sum of counts, offsets[E] = S int32 [E+1]
+ *  sorted_slots[p] slot at sorted position p                      int32 [S]
+ *  pos_of_slot[s]  sorted position of slot s (inverse)            int32 [S]
+ * Every topk_ids entry must lie in [0, E).  ws/ws_bytes: unused (pass NULL, 0);
+ * kept so the call can grow a workspace without an ABI change.
+ */
+int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                  int32_t* sorted_slots, int32_t* pos_of_slot, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
+ * One stage of every routed expert's FFN over its group of slots.
+ *  stage APMOE_GATE_UP_SWIGLU (optionally | APMOE_ONLY_GEMV or | APMOE_ONLY_TILE):
+ *        in = x fp16 [T][H]; the row for sorted position
+ *        p is x[sorted_slots[p] / k]; out = A fp16 [S][I] in sorted order,
+ *        A = silu(W_gate x) * (W_up x), with g, u and silu in fp32.
+ *  stage APMOE_DOWN: in = A fp16 [S][I] (sorted order); out = Y fp32 [S][H]
+ *        in sorted order, Y = W_down a.
+ *  experts  device array of E descriptors
+ *  bits     int8 [E] on the device, each in {3,4,5,6,16}, read by the kernels
+ *           (see apmoe_commit_bits); experts with no slots read no weights.
+ *  offsets  int32 [E+1] from apmoe_permute; sorted_slots int32 [S].
+ *  mfma_min_tokens  groups with at least this many slots take the dequantise-
+ *           to-LDS + MFMA tile path, smaller ones the bit-plane GEMV path
+ *           (both paths give results within the same tolerance).  >= 1.
+ *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I).
+ * The dispatch reads counts and bitwidths on the device: no host sync.
+ * An always-on shared expert is the same call with E = 1, bits = {16},
+ * offsets = {0, T}, sorted_slots = 0..T-1 and k = 1.
+ */
+int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, const int8_t* bits, int E,
+                            const int32_t* offsets, const int32_t* sorted_slots, int k,
+                            const uint16_t* in, void* out, int T, int H, int I,
+                            int mfma_min_tokens, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine: out[t][h] = sum_{j=0..k-1} topk_w[t][j] * Y[pos_of_slot[t*k+j]][h]
+ * (+ y_shared[t][h]), summed in fp32 in ascending j, rounded once to fp16.
+ *  Y fp32 [S][H] (sorted order); y_shared fp32 [T][H] or NULL; out fp16 [T][H].
+ */
+int apmoe_combine(const float* Y, const int32_t* pos_of_slot, const float* topk_w, int T, int k,
+                  int H, const float* y_shared, uint16_t* out, void* stream);
+
+/*
+ * Greedy bitwidth planner (host only, touches no GPU).  Starting from every
+ * expert at levels[0], it repeatedly lowers by one level the expert, not yet
+ * at its floor, whose step costs the least harm per byte saved,
+ * (harm[e][l+1] - harm[e][l]) / (bytes[e][l] - bytes[e][l+1]), ties to the
+ * larger saving and then the lower index, until the plan fits the budget.
+ *  levels    [host] int8 [L] bitwidths from high to low, e.g. {16,6,5,4,3}
+ *  harm      [host] double [E][L]   bytes [host] uint64 [E][L] strictly decreasing in l
+ *  floor_bits[host] int8 [E], each one of levels
+ *  bits_out  [host] int8 [E]
+ * Returns APMOE_ENOSPACE with bits_out = the floors when even the floors do
+ * not fit; APMOE_EINVAL / APMOE_EBITS for malformed inputs.
+ */
+int apmoe_plan_bitwidths(int E, int L, const int8_t* levels, const double* harm,
+                         const uint64_t* bytes, const int8_t* floor_bits, uint64_t budget,
+                         int8_t* bits_out);
+
+/*
+ * Commit a plan at a safe boundary: validates bits_host [host] int8 [E] and
+ * enqueues its copy into bits_dev on `stream`, so layer calls enqueued before
+ * it see the old bitwidths and calls enqueued after it see the new ones.  The
+ * values travel as kernel arguments: bits_host may be reused on return.
+ */
+int apmoe_commit_bits(const int8_t* bits_host, int E, int8_t* bits_dev, void* stream);
+
+/* Workspace bytes apmoe_bitplane_lut_gemm needs for these shapes. */
+size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I);
+
+/* Static description of an error code. */
+const char* apmoe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* APMOE_H */

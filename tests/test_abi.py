@@ -1,0 +1,106 @@
+"""Host-side checks of libapmoe: it loads, exports every entry point the header
+declares, validates arguments before touching the GPU, and its host planner
+agrees bit-exactly with the planner oracle.  No GPU compute is called."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+from any_precision_quantized_amd import _lib
+from oracle import planner as planner_ref
+
+
+def test_library_exports_header_symbols():
+    lib = _lib._lib()
+    names = _lib.header_symbols()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", _lib.HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_strerror():
+    for code in (0, -1, -2, -3, -4, -99):
+        assert isinstance(_lib.strerror(code), str) and _lib.strerror(code)
+
+
+def test_validation_before_launch():
+    lib = _lib._lib()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    # route: k > E, bad scale, null pointers
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 9, fake, fake, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 0.0, 8, 2, fake, fake, None) == _lib.EINVAL
+    assert lib.apmoe_route(None, 4, 64, fake, None, 1.0, 8, 2, fake, fake, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 300, 2, fake, fake, None) == _lib.EINVAL
+    assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None) == _lib.OK   # T = 0
+    # permute
+    assert lib.apmoe_permute(fake, 4, 0, 8, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(None, 4, 2, 8, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(None, 0, 2, 8, None, None, None, None, None, 0, None) == _lib.OK
+    # gemm: bad stage, H or I not a multiple of 32, mfma_min_tokens < 1
+    g = lib.apmoe_bitplane_lut_gemm
+    assert g(7, fake, fake, 8, fake, fake, 2, fake, fake, 4, 64, 64, 16, None, 0, None) == _lib.EINVAL
+    assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, 4, 65, 64, 16, None, 0, None) == _lib.EINVAL
+    assert g(1, fake, fake, 8, fake, fake, 2, fake, fake, 4, 64, 48, 16, None, 0, None) == _lib.EINVAL
+    assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, 4, 64, 64, 0, None, 0, None) == _lib.EINVAL
+    assert g(0, fake, fake, 8, fake, None, 2, fake, fake, 4, 64, 64, 16, None, 0, None) == _lib.EINVAL
+    assert g(0, None, None, 8, None, None, 2, None, None, 0, 64, 64, 16, None, 0, None) == _lib.OK
+    # combine
+    assert lib.apmoe_combine(fake, fake, fake, 4, 2, 48, None, fake, None) == _lib.EINVAL
+    assert lib.apmoe_combine(None, fake, fake, 4, 2, 64, None, fake, None) == _lib.EINVAL
+    # commit: invalid bitwidth rejected on the host
+    bad = (ctypes.c_int8 * 3)(6, 7, 3)
+    assert lib.apmoe_commit_bits(bad, 3, fake, None) == _lib.EBITS
+    assert lib.apmoe_commit_bits(bad, 0, fake, None) == _lib.EINVAL
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_host_planner_matches_oracle(seed):
+    rng = np.random.default_rng(100 + seed)
+    levels = [16, 6, 5, 4, 3] if seed % 2 else [6, 5, 4, 3]
+    E = int(rng.integers(1, 40))
+    L = len(levels)
+    size = rng.integers(1000, 10**7, size=E)
+    nb = np.array([[int(s * b / 16) + 31 for b in levels] for s in size], dtype=np.uint64)
+    harm = np.cumsum(rng.random((E, L)), axis=1) * rng.random((E, 1))
+    harm -= harm[:, :1]
+    if seed % 3 == 0:
+        harm = np.round(harm, 1)          # many exact ties in cost
+    floors = np.array([rng.choice(levels[1:]) for _ in range(E)], dtype=np.int8)
+    lo = planner_ref.plan_total(levels, nb, floors)
+    hi = planner_ref.plan_total(levels, nb, [levels[0]] * E)
+    for budget in list(np.linspace(lo, hi, 9).astype(np.int64)) + [lo - 1]:
+        st_ref, bits_ref = planner_ref.plan_bitwidths(levels, harm, nb, floors, int(budget))
+        st, bits = _lib.plan_bitwidths(levels, harm, nb, floors, int(budget))
+        assert st == st_ref
+        assert np.array_equal(bits, bits_ref)
+
+
+def test_host_planner_zipf_plan():
+    cfg = synth.get("qwen_decode")
+    p = synth.gen.zipf_prior(cfg.E, cfg.zipf_s)
+    plan = synth.planner_inputs(cfg, p)
+    args = (plan["levels"], plan["harm"], plan["bytes"], plan["floors"], plan["budget"])
+    st, bits = _lib.plan_bitwidths(*args)
+    st_ref, bits_ref = planner_ref.plan_bitwidths(*args)
+    assert st == st_ref == 0
+    assert np.array_equal(bits, bits_ref)
+
+
+def test_host_planner_rejects_bad_inputs():
+    st, _ = _lib.plan_bitwidths([6, 7, 4], np.zeros((2, 3)), np.array([[3, 2, 1]] * 2), [4, 4], 10)
+    assert st == _lib.EBITS
+    st, _ = _lib.plan_bitwidths([6, 5, 4], np.zeros((2, 3)), np.array([[3, 3, 1]] * 2), [4, 4], 10)
+    assert st == _lib.EINVAL
+    st, _ = _lib.plan_bitwidths([6, 5, 4], np.zeros((2, 3)), np.array([[3, 2, 1]] * 2), [3, 4], 10)
+    assert st == _lib.EINVAL

@@ -1,0 +1,134 @@
+"""GPU parity of every step of the layer against the oracle, through the C ABI.
+
+Bars: routing ids, counts, offsets, sorted slots and their inverse bit-exact
+(ids outside the near-tie guard); gates within 1e-6; A, Y and the layer
+output within |y - y_ref| <= 2e-3 * sum|w||x| + 1e-5 per element.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from any_precision_quantized_amd import _lib
+from oracle import moe
+
+from . import gpu_helpers as G
+from .oracle_cache import layer_ref, prefill_tokens, resolve_bits
+
+pytestmark = pytest.mark.gpu
+
+ALL_GEMV = 1 << 30     # every group on the bit-plane GEMV path
+ALL_TILE = 1           # every group on the MFMA tile path
+
+SMALL = {
+    "tiny": synth.get("tiny"),
+    # ragged: H = 10 words, I = 26 row-groups of 16 (not a multiple of 64), odd T
+    "ragged": synth.custom("ragged", E=6, H=320, I=416, k=2, T=37, bits=(3, 4, 5, 6, 16, 4)),
+    # k = E and tiny K (3 words)
+    "k_eq_e": synth.custom("k_eq_e", E=5, H=96, I=96, k=5, T=7, bits=(6, 3, 16, 5, 4)),
+    # one expert, 50 tokens: a single group crossing the tile threshold
+    "one_expert": synth.custom("one_expert", E=1, H=128, I=224, k=1, T=50, bits=(5,)),
+    # every expert on the fp16 fallback
+    "all_fp16": synth.custom("all_fp16", E=4, H=256, I=160, k=2, T=21, bits=(16, 16, 16, 16)),
+    # a single token
+    "t1": synth.custom("t1", E=8, H=512, I=384, k=2, T=1, bits=(3, 4, 5, 6, 16, 3, 4, 5)),
+    # 128 tokens over 3 experts: groups of ~85 (several 64-token tiles, ragged)
+    "wide": synth.custom("wide", E=3, H=192, I=288, k=2, T=128, bits=(4, 6, 3)),
+}
+
+
+@pytest.mark.parametrize("mfma_min", [ALL_GEMV, ALL_TILE, 16])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_every_step(name, mfma_min):
+    cfg = SMALL[name]
+    G.say(f"case {name} mfma_min {mfma_min}")
+    inp = G.inputs(cfg)
+    bits = resolve_bits(inp)
+    ref = moe.layer(inp, bits=bits)
+    _, got = G.run_layer(inp, bits, mfma_min)
+    n_amb = G.check_route(inp, got, ref["ids"], ref["gates"], ref["logits"])
+    assert n_amb == 0
+    G.check_grouping(cfg, got)
+    worst = G.check_experts(inp, bits, got)
+    ratio = G.check_out(got, ref)
+    G.say(f"  worst expert err/bound {worst:.3g}, layer err/bound {ratio:.3g}")
+
+
+def test_forced_single_expert_skew():
+    cfg = synth.custom("skew", E=4, H=128, I=96, k=1, T=100, bits=(3, 6, 4, 16))
+    inp = dataclasses.replace(G.inputs(cfg), bias=np.array([-100, -100, 100, -100], dtype=np.float32))
+    ref = moe.layer(inp)
+    for mfma_min in (ALL_GEMV, ALL_TILE):
+        _, got = G.run_layer(inp, inp.bits, mfma_min)
+        assert got["counts"].tolist() == [0, 0, 100, 0]
+        G.check_route(inp, got, ref["ids"], ref["gates"], ref["logits"])
+        G.check_grouping(cfg, got)
+        G.check_out(got, ref)
+
+
+def test_deterministic_bitwise():
+    inp = G.inputs(SMALL["ragged"])
+    bits = inp.bits
+    for mfma_min in (ALL_GEMV, ALL_TILE):
+        layer, a = G.run_layer(inp, bits, mfma_min)
+        _, b = G.run_layer(inp, bits, mfma_min, layer=layer)
+        for key in ("ids", "gates", "sorted_slots", "A", "Y", "out"):
+            assert np.array_equal(a[key], b[key]), key
+
+
+def test_commit_takes_effect_in_stream_order():
+    import torch
+    from any_precision_quantized_amd import layer as L
+    inp = G.inputs(SMALL["tiny"])
+    bits1 = np.array(inp.bits)
+    bits2 = np.array([6, 6, 3, 3, 16, 5, 4, 3], dtype=np.int8)
+    for e in range(8):
+        if bits2[e] == 16 and inp.experts[e]["gate"].w16 is None:
+            bits2[e] = 4        # tiny has no fp16 copies
+    layer = L.from_inputs(inp, bits=bits1)
+    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.float16)
+    out1 = layer.forward(x).clone()          # enqueued before the commit
+    layer.commit(bits2)
+    out2 = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    r1, r2 = moe.layer(inp, bits=bits1), moe.layer(inp, bits=bits2)
+    G.check_out({"out": out1.float().cpu().numpy()}, r1)
+    G.check_out({"out": out2.float().cpu().numpy()}, r2)
+
+
+def test_commit_rejects_invalid_bits():
+    import torch
+    dev = torch.zeros(4, dtype=torch.int8, device="cuda")
+    with pytest.raises(_lib.ApmoeError):
+        _lib.commit_bits([3, 4, 7, 6], dev)
+    torch.cuda.synchronize()
+    assert dev.cpu().tolist() == [0, 0, 0, 0]
+
+
+# ---------------------------------------------------------------------------
+# The published workloads at full size
+# ---------------------------------------------------------------------------
+
+FULL = ["tiny", "qwen_decode", "mixtral_decode_t1", "mixtral_decode_t8", "mixtral_decode_t32",
+        "e128_decode", "mixtral_prefill"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_layer(name):
+    cfg = synth.get(name)
+    G.say(f"full-size case {name}")
+    inp = G.inputs(cfg)
+    bits = resolve_bits(inp)
+    tokens = prefill_tokens(cfg.T) if cfg.T > 1024 else None
+    ref = layer_ref(inp, bits, tokens)
+    _, got = G.run_layer(inp, bits)
+    n_amb = G.check_route(inp, got, ref["ids"], ref["gates"], ref["logits"])
+    G.check_grouping(cfg, got)
+    ratio = G.check_out(got, ref, tokens)
+    # per-expert isolation on two touched experts (hottest and coldest) of the smaller shapes
+    touched = [e for e in range(cfg.E) if got["counts"][e] > 0]
+    if cfg.H * cfg.I <= 2048 * 2048:
+        G.check_experts(inp, bits, got, experts=[touched[0], touched[-1]])
+    G.say(f"  ambiguous routes {n_amb}, layer err/bound {ratio:.3g}, "
+          f"groups {sorted(got['counts'].tolist(), reverse=True)[:8]}")
