@@ -51,6 +51,8 @@ def _lib():
             "apmoe_plan_bitwidths": [_c_int, _c_int, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp],
             "apmoe_commit_bits": [_vp, _c_int, _vp, _vp],
             "apmoe_workspace_bytes": [_c_int, _c_int, _c_int, _c_int, _c_int],
+            "apmoe_packed_plane_words": [_c_int, _c_int],
+            "apmoe_pack_planes": [_vp, _c_int, _c_int, _vp, _vp],
             "apmoe_strerror": [_c_int],
         }
         for name, args in sig.items():
@@ -58,6 +60,7 @@ def _lib():
             fn.argtypes = args
             fn.restype = _c_int
         lib.apmoe_workspace_bytes.restype = _c_size
+        lib.apmoe_packed_plane_words.restype = _c_size
         lib.apmoe_strerror.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
@@ -139,6 +142,19 @@ def permute(topk_ids, E, counts, offsets, sorted_slots, pos_of_slot, stream=None
 
 def workspace_bytes(T, k, E, H, I) -> int:
     return int(_lib().apmoe_workspace_bytes(T, k, E, H, I))
+
+
+def packed_plane_words(rows, cols) -> int:
+    return int(_lib().apmoe_packed_plane_words(rows, cols))
+
+
+def pack_planes(src, rows, cols, dst, stream=None):
+    """Canonical planes (device int32 view of uint32 [6, rows, cols/32]) -> packed layout."""
+    torch = _torch()
+    rc = _lib().apmoe_pack_planes(_ptr(src, torch.int32, 6 * rows * (cols // 32), "planes"), rows, cols,
+                                  _ptr(dst, torch.int32, packed_plane_words(rows, cols), "packed"),
+                                  _stream(stream))
+    _check(rc, "apmoe_pack_planes")
 
 
 def bitplane_lut_gemm(stage, experts_desc, bits, E, offsets, sorted_slots, k, inp, out, T, H, I,

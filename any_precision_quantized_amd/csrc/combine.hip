@@ -24,6 +24,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<half4_t*>(out + (size_t)t * H + h) = o;
 }
 
+// Canonical [6][rows][W] planes -> packed layout (one output word per thread,
+// so the writes are contiguous).
+__global__ __launch_bounds__(256) void pack_planes_kernel(const uint32_t* __restrict__ src, int rows, int cols,
+                                                          uint32_t* __restrict__ dst) {
+    const int W = cols / 32;
+    const int nsteps = packed_steps(cols);
+    const size_t slab = packed_slab_words(rows, cols);
+    const size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (o >= 6 * slab) return;
+    const int p = (int)(o / slab);
+    const size_t rem = o % slab;
+    const int rg = (int)(rem / ((size_t)nsteps * 64));
+    const int r2 = (int)(rem % ((size_t)nsteps * 64));
+    const int s = r2 / 64, l = r2 % 64;
+    const int w = 4 * s + l / 16;
+    const int row = 16 * rg + l % 16;
+    dst[o] = w < W ? src[((size_t)p * rows + row) * W + w] : 0u;
+}
+
 struct BitsArg {
     int8_t v[APMOE_MAX_EXPERTS];
 };
@@ -61,12 +80,27 @@ extern "C" int apmoe_commit_bits(const int8_t* bits_host, int E, int8_t* bits_de
 }
 
 extern "C" size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I) {
-    (void)T;
-    (void)k;
-    (void)E;
-    (void)H;
-    (void)I;
-    return 0;
+    if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
+    const size_t gu = gemv_workspace_bytes(T, k, E, I, H, 2);
+    const size_t dn = gemv_workspace_bytes(T, k, E, H, I, 1);
+    return gu > dn ? gu : dn;
+}
+
+extern "C" size_t apmoe_packed_plane_words(int rows, int cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return 6 * packed_slab_words(rows, cols);
+}
+
+extern "C" int apmoe_pack_planes(const uint32_t* src, int rows, int cols, uint32_t* dst, void* stream) {
+    if (!src || !dst || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return APMOE_EINVAL;
+    const size_t n = apmoe_packed_plane_words(rows, cols);
+    const char* s0 = reinterpret_cast<const char*>(src);
+    const char* d0 = reinterpret_cast<const char*>(dst);
+    const size_t sb = (size_t)6 * rows * (cols / 32) * 4, db = n * 4;
+    if (s0 < d0 + db && d0 < s0 + sb) return APMOE_EINVAL;   // overlapping buffers
+    hipLaunchKernelGGL(pack_planes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), src,
+                       rows, cols, dst);
+    return launch_status();
 }
 
 extern "C" const char* apmoe_strerror(int code) {

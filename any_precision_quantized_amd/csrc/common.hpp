@@ -43,6 +43,48 @@ inline int launch_status() {
     return e == hipSuccess ? APMOE_OK : APMOE_EHIP;
 }
 
+// b-bit code of column i (0..31) of a word from the top b plane words.
+__device__ inline int code_of(const uint32_t* w, int b, int i) {
+    int c = 0;
+    for (int p = 0; p < b; ++p) c = (c << 1) | ((w[p] >> i) & 1u);
+    return c;
+}
+
+// Pointers read out of the device-side descriptor table are generic; these
+// global-address-space views let loads through them be global (not flat)
+// loads, which count only against vmcnt and so never stall LDS waits.
+typedef __attribute__((address_space(1))) const uint32_t gu32_t;
+typedef __attribute__((address_space(1))) const half_t gh16_t;
+typedef __attribute__((address_space(1))) const uint16_t gu16_t;
+
+__device__ inline half8_t load_h8g(gh16_t* p) {
+    return *reinterpret_cast<__attribute__((address_space(1))) const half8_t*>(p);
+}
+
+struct MatView {
+    gu32_t* planes;   // plane p of row r, word w: planes[(p * rows + r) * W + w]
+    gh16_t* lut;      // [rows][1 << b]
+    gh16_t* w16;      // [rows][K]
+};
+
+__device__ inline MatView mat_view(const apmoe_mat& m, int b) {
+    MatView v;
+    v.planes = (gu32_t*)m.planes;
+    v.lut = (b >= 3 && b <= 6) ? (gh16_t*)m.lut[b - 3] : nullptr;
+    v.w16 = (gh16_t*)m.w16;
+    return v;
+}
+
+// Packed plane layout: inside each plane slab, the words of 16-row group rg
+// are ordered [step][g][i] = canonical word 4*step + g of row 16*rg + i.
+__host__ __device__ inline int packed_steps(int cols) { return (cols / 32 + 3) / 4; }
+__host__ __device__ inline size_t packed_slab_words(int rows, int cols) {
+    return (size_t)rows * 4 * packed_steps(cols);
+}
+__device__ inline size_t packed_index(int rows, int nsteps, int p, int row, int w) {
+    return (size_t)p * rows * 4 * nsteps + ((size_t)(row >> 4) * nsteps + (w >> 2)) * 64 + (w & 3) * 16 + (row & 15);
+}
+
 // Internal launchers of the two expert-FFN paths (apmoe_bitplane_lut_gemm).
 struct GemmArgs {
     int stage;
@@ -58,7 +100,8 @@ struct GemmArgs {
     int mfma_min_tokens;
 };
 
-int launch_gemv(const GemmArgs& a, hipStream_t s);
+int launch_gemv(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+size_t gemv_workspace_bytes(int T, int k, int E, int rows, int K, int nmat);
 int launch_tile(const GemmArgs& a, hipStream_t s);
 
 }  // namespace apmoe

@@ -1,4 +1,5 @@
-// Expert FFN stages over bit-plane + LUT weights: apmoe_bitplane_lut_gemm.
+// Expert FFN stages over bit-plane + LUT weights: apmoe_bitplane_lut_gemm,
+// and its dequantise-to-LDS + MFMA tile path (groups of >= mfma_min_tokens).
 //
 // Dispatch happens on the device: every workgroup reads its expert's slot
 // count and bitwidth and leaves at once when the group is empty or belongs to
@@ -6,123 +7,6 @@
 #include "common.hpp"
 
 namespace apmoe {
-
-// ---------------------------------------------------------------------------
-// Weight decode helpers
-// ---------------------------------------------------------------------------
-
-// b-bit code of column i (0..31) of a word from the top b plane words.
-__device__ inline int code_of(const uint32_t* w, int b, int i) {
-    int c = 0;
-    for (int p = 0; p < b; ++p) c = (c << 1) | ((w[p] >> i) & 1u);
-    return c;
-}
-
-struct MatView {
-    const uint32_t* planes;  // plane p of row r, word w: planes[(p * rows + r) * W + w]
-    const half_t* lut;       // [rows][1 << b]
-    const half_t* w16;       // [rows][K]
-};
-
-__device__ inline MatView mat_view(const apmoe_mat& m, int b) {
-    MatView v;
-    v.planes = m.planes;
-    v.lut = (b >= 3 && b <= 6) ? reinterpret_cast<const half_t*>(m.lut[b - 3]) : nullptr;
-    v.w16 = reinterpret_cast<const half_t*>(m.w16);
-    return v;
-}
-
-// ---------------------------------------------------------------------------
-// GEMV path (groups below mfma_min_tokens): one wave per output row, lanes
-// stride over the plane words of the row, fp32 accumulate, butterfly reduce.
-// ---------------------------------------------------------------------------
-
-constexpr int kGemvRows = 16;   // rows per workgroup (4 waves x 4 rows)
-constexpr int kGemvMT = 8;      // tokens per pass over a row
-
-template <int NMAT>
-__global__ __launch_bounds__(256) void gemv_simple_kernel(GemmArgs a, int row_blocks) {
-    const int e = blockIdx.x / row_blocks;
-    const int rb = blockIdx.x % row_blocks;
-    const int off = a.offsets[e];
-    const int m = a.offsets[e + 1] - off;
-    if (m == 0 || m >= a.mfma_min_tokens) return;
-    const int b = a.bits[e];
-    if (!valid_bits(b)) return;  // the table is validated on commit; never decode past plane 5
-    const int rows = NMAT == 2 ? a.I : a.H;
-    const int K = NMAT == 2 ? a.H : a.I;
-    const int W = K / 32;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const half_t* in = reinterpret_cast<const half_t*>(a.in);
-
-    MatView mv[NMAT];
-    if (NMAT == 2) {
-        mv[0] = mat_view(a.experts[e].gate, b);
-        mv[NMAT - 1] = mat_view(a.experts[e].up, b);
-    } else {
-        mv[0] = mat_view(a.experts[e].down, b);
-    }
-
-    for (int r = rb * kGemvRows + wave; r < min(rows, (rb + 1) * kGemvRows); r += 4) {
-        for (int t0 = 0; t0 < m; t0 += kGemvMT) {
-            const int mt = min(kGemvMT, m - t0);
-            const half_t* xrow[kGemvMT];
-            for (int t = 0; t < kGemvMT; ++t) {
-                const int j = off + t0 + min(t, mt - 1);
-                xrow[t] = NMAT == 2 ? in + (size_t)(a.sorted_slots[j] / a.k) * K : in + (size_t)j * K;
-            }
-            float acc[NMAT][kGemvMT];
-            for (int q = 0; q < NMAT; ++q)
-                for (int t = 0; t < kGemvMT; ++t) acc[q][t] = 0.f;
-            for (int w = lane; w < W; w += kWave) {
-                float wt[NMAT][32];
-                for (int q = 0; q < NMAT; ++q) {
-                    if (b == 16) {
-                        const half_t* src = mv[q].w16 + (size_t)r * K + 32 * w;
-                        for (int i = 0; i < 32; ++i) wt[q][i] = (float)src[i];
-                    } else {
-                        uint32_t pw[6];
-                        for (int p = 0; p < b; ++p) pw[p] = mv[q].planes[((size_t)p * rows + r) * W + w];
-                        const half_t* lut = mv[q].lut + (size_t)r * (1 << b);
-                        for (int i = 0; i < 32; ++i) wt[q][i] = (float)lut[code_of(pw, b, i)];
-                    }
-                }
-                for (int t = 0; t < kGemvMT; ++t) {
-                    if (t >= mt) break;
-                    const half_t* xs = xrow[t] + 32 * w;
-                    for (int i = 0; i < 32; ++i) {
-                        const float xv = (float)xs[i];
-                        for (int q = 0; q < NMAT; ++q) acc[q][t] = fmaf(wt[q][i], xv, acc[q][t]);
-                    }
-                }
-            }
-            for (int t = 0; t < kGemvMT; ++t) {
-                float s[NMAT];
-                for (int q = 0; q < NMAT; ++q) s[q] = wave_sum(acc[q][t]);
-                if (lane == 0 && t < mt) {
-                    const int j = off + t0 + t;
-                    if (NMAT == 2) {
-                        reinterpret_cast<half_t*>(a.out)[(size_t)j * rows + r] =
-                            (half_t)(silu_f32(s[0]) * s[NMAT - 1]);
-                    } else {
-                        reinterpret_cast<float*>(a.out)[(size_t)j * rows + r] = s[0];
-                    }
-                }
-            }
-        }
-    }
-}
-
-int launch_gemv(const GemmArgs& a, hipStream_t s) {
-    const int rows = a.stage == APMOE_GATE_UP_SWIGLU ? a.I : a.H;
-    const int row_blocks = (rows + kGemvRows - 1) / kGemvRows;
-    dim3 grid(a.E * row_blocks);
-    if (a.stage == APMOE_GATE_UP_SWIGLU)
-        hipLaunchKernelGGL(gemv_simple_kernel<2>, grid, dim3(256), 0, s, a, row_blocks);
-    else
-        hipLaunchKernelGGL(gemv_simple_kernel<1>, grid, dim3(256), 0, s, a, row_blocks);
-    return launch_status();
-}
 
 // ---------------------------------------------------------------------------
 // Tile path (groups of at least mfma_min_tokens): the weight tile is decoded
@@ -140,18 +24,23 @@ __global__ __launch_bounds__(256) void tile_simple_kernel(GemmArgs a) {
     const int W = K / 32;
     const int n0 = blockIdx.x * kBN;
 
-    // Map blockIdx.y to (expert, m-tile) over the groups that take this path.
-    int q = blockIdx.y, e = -1, m0 = 0, off = 0, m = 0;
+    // Map blockIdx.y to (expert, m-tile) over the groups that take this path
+    // (slot counts staged in LDS once, then a scan from LDS).
+    __shared__ int cnt[APMOE_MAX_EXPERTS + 1];
+    for (int ee = threadIdx.x; ee <= a.E; ee += blockDim.x) cnt[ee] = a.offsets[ee];
+    __syncthreads();
+    for (int slot = blockIdx.y; slot < a.T * a.k / kBM + a.E; slot += gridDim.y) {
+    int q = slot, e = -1, m0 = 0, off = 0, m = 0;
     for (int ee = 0; ee < a.E; ++ee) {
-        const int o = a.offsets[ee], c = a.offsets[ee + 1] - o;
+        const int o = cnt[ee], c = cnt[ee + 1] - o;
         if (c < a.mfma_min_tokens || c == 0) continue;
         const int tiles = (c + kBM - 1) / kBM;
         if (q < tiles) { e = ee; m0 = q * kBM; off = o; m = c; break; }
         q -= tiles;
     }
-    if (e < 0) return;
+    if (e < 0) break;   // slots past the last tile: uniform over the workgroup
     const int b = a.bits[e];
-    if (!valid_bits(b)) return;
+    if (!valid_bits(b)) continue;
     MatView mv[NMAT];
     if (NMAT == 2) {
         mv[0] = mat_view(a.experts[e].gate, b);
@@ -192,11 +81,11 @@ __global__ __launch_bounds__(256) void tile_simple_kernel(GemmArgs a) {
             half8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
             if (wrow < rows) {
                 if (b == 16) {
-                    v = *reinterpret_cast<const half8_t*>(mv[qq].w16 + (size_t)wrow * K + 32 * kw + lc);
+                    v = load_h8g(mv[qq].w16 + (size_t)wrow * K + 32 * kw + lc);
                 } else {
                     uint32_t pw[6];
-                    for (int p = 0; p < b; ++p) pw[p] = mv[qq].planes[((size_t)p * rows + wrow) * W + kw];
-                    const half_t* lut = mv[qq].lut + (size_t)wrow * (1 << b);
+                    for (int p = 0; p < b; ++p) pw[p] = mv[qq].planes[packed_index(rows, packed_steps(K), p, wrow, kw)];
+                    gh16_t* lut = mv[qq].lut + (size_t)wrow * (1 << b);
                     for (int i = 0; i < 8; ++i) v[i] = lut[code_of(pw, b, lc + i)];
                 }
             }
@@ -235,6 +124,8 @@ __global__ __launch_bounds__(256) void tile_simple_kernel(GemmArgs a) {
                         reinterpret_cast<float*>(a.out)[o] = acc[0][i][j][r];
                 }
             }
+    __syncthreads();
+    }
 }
 
 int launch_tile(const GemmArgs& a, hipStream_t s) {
@@ -242,7 +133,7 @@ int launch_tile(const GemmArgs& a, hipStream_t s) {
     if (S < a.mfma_min_tokens) return APMOE_OK;  // no group can reach the threshold
     const int rows = a.stage == APMOE_GATE_UP_SWIGLU ? a.I : a.H;
     const int mslots = (S + kBM - 1) / kBM + a.E;
-    dim3 grid((rows + kBN - 1) / kBN, mslots);
+    dim3 grid((rows + kBN - 1) / kBN, mslots < 16 ? mslots : 16);
     if (a.stage == APMOE_GATE_UP_SWIGLU)
         hipLaunchKernelGGL(tile_simple_kernel<2>, grid, dim3(256), 0, s, a);
     else
@@ -269,11 +160,10 @@ extern "C" int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, c
     if (!experts || !bits || !offsets || !in || !out) return APMOE_EINVAL;
     if (stage == APMOE_GATE_UP_SWIGLU && !sorted_slots) return APMOE_EINVAL;
     if (ws_bytes < apmoe_workspace_bytes(T, k, E, H, I)) return APMOE_ENOSPACE;
-    (void)ws;
     GemmArgs a{stage, experts, bits, E, offsets, sorted_slots, k, in, out, T, H, I, mfma_min_tokens};
     hipStream_t s = as_stream(stream);
     if (paths != APMOE_ONLY_TILE) {
-        const int rc = launch_gemv(a, s);
+        const int rc = launch_gemv(a, ws, ws_bytes, s);
         if (rc != APMOE_OK) return rc;
     }
     if (paths != APMOE_ONLY_GEMV) return launch_tile(a, s);

@@ -19,16 +19,19 @@ from . import _lib
 
 MATS = ("gate", "up", "down")
 DESC_WORDS = 18          # 3 matrices x (planes, lut[4], w16) pointers
-# Groups of at least this many slots take the dequantise-to-LDS + MFMA tile path.
-DEFAULT_MFMA_MIN_TOKENS = 16
+# Groups of at least this many slots take the dequantise-to-LDS + MFMA tile path;
+# smaller ones take the bit-plane GEMV path (one pass over K covers 64 tokens).
+DEFAULT_MFMA_MIN_TOKENS = 65   # a group of up to 64 slots is one GEMV pass
 
 
 class ExpertTable:
     """Expert weights in device memory plus their descriptor array.
 
     ``experts``: sequence of mappings name -> matrix, each matrix exposing
-    ``planes`` (uint32 [6, rows, cols/32]), ``luts`` (four fp16 arrays
-    [rows, 2**b]) and ``w16`` (fp16 [rows, cols] or None).
+    ``planes`` (canonical uint32 [6, rows, cols/32]), ``luts`` (four fp16
+    arrays [rows, 2**b]) and ``w16`` (fp16 [rows, cols] or None).  The planes
+    are repacked once on the device into the layout the kernels read
+    (apmoe_pack_planes).
     """
 
     def __init__(self, experts, device="cuda", _tensors=None):
@@ -43,7 +46,13 @@ class ExpertTable:
                     m = mats[name]
                     ent = {"planes": None, "luts": [None] * 4, "w16": None}
                     if m.planes is not None and m.planes.size:
-                        ent["planes"] = torch.from_numpy(np.ascontiguousarray(m.planes).view(np.int32)).to(device)
+                        # canonical planes in, kernel-native packed planes kept
+                        canon = torch.from_numpy(np.ascontiguousarray(m.planes).view(np.int32)).to(device)
+                        rows, cols = m.planes.shape[1], m.planes.shape[2] * 32
+                        packed = torch.empty(_lib.packed_plane_words(rows, cols), dtype=torch.int32, device=device)
+                        _lib.pack_planes(canon, rows, cols, packed)
+                        ent["planes"] = packed
+                        del canon
                     for i, lut in enumerate(m.luts or []):
                         ent["luts"][i] = torch.from_numpy(np.ascontiguousarray(lut).view(np.int16)).to(device)
                     if m.w16 is not None:
@@ -117,8 +126,10 @@ class MoELayer:
         self.A = torch.empty((S, I), dtype=torch.float16, **dev)
         self.Y = torch.empty((S, H), dtype=torch.float32, **dev)
         self.out = torch.empty((T, H), dtype=torch.float16, **dev)
-        nws = _lib.workspace_bytes(T, k, E, H, max(I, shared_I or 0))
-        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, **dev) if nws else None
+        nws = _lib.workspace_bytes(T, k, E, H, I)
+        if shared_I:
+            nws = max(nws, _lib.workspace_bytes(T, 1, 1, H, shared_I))
+        self.ws = torch.empty(nws, dtype=torch.uint8, **dev) if nws else None
         self.shared = shared
         self.shared_I = shared_I
         if shared is not None:

@@ -54,10 +54,18 @@ extern "C" {
 
 /*
  * One weight matrix W [rows x cols], cols = the contraction dimension K.
- *  planes : uint32 [6][rows][cols/32]; plane 0 holds the most significant bit
- *           of each weight's 6-bit code; bit i of word w is column 32*w + i.
- *           A b-bit expert reads only planes 0..b-1 (its code is the top b
- *           bits of the 6-bit code).  Plane-major, so each plane is one slab.
+ * Two layouts of the six uint32 bit-planes exist:
+ *  - canonical (interchange): planes[p][row][w], plane 0 = most significant
+ *    bit of each weight's 6-bit code, bit i of word w = column 32*w + i;
+ *    a b-bit code is the top b planes.  This is what checkpoints, the
+ *    generator and the CPU oracle use.
+ *  - packed (what the kernels read, from apmoe_pack_planes): every plane is
+ *    still its own slab, so a b-bit expert reads only planes 0..b-1, but
+ *    inside a slab the words of each 16-row group are ordered
+ *    [step][g][i] = canonical word 4*step + g of row 16*group + i, with
+ *    nsteps = ceil(cols/128) steps (missing words zero).  One slab holds
+ *    rows * 4 * nsteps words; one GPU load then reads 256 contiguous bytes.
+ *  planes : packed uint32 planes (see apmoe_packed_plane_words).
  *  lut[b-3]: fp16 [rows][1 << b], the b-bit centroid table of every row.
  *  w16    : fp16 [rows][cols] plain weights, read only when the expert runs
  *           at bitwidth 16; may be NULL for experts that never do.
@@ -115,7 +123,9 @@ int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
  *  mfma_min_tokens  groups with at least this many slots take the dequantise-
  *           to-LDS + MFMA tile path, smaller ones the bit-plane GEMV path
  *           (both paths give results within the same tolerance).  >= 1.
- *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I).
+ *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I)
+ *           bytes (split-K partial sums; 0 for shapes that never split K).
+ *           Calls that share one workspace must not overlap.
  * The dispatch reads counts and bitwidths on the device: no host sync.
  * An always-on shared expert is the same call with E = 1, bits = {16},
  * offsets = {0, T}, sorted_slots = 0..T-1 and k = 1.
@@ -160,6 +170,18 @@ int apmoe_commit_bits(const int8_t* bits_host, int E, int8_t* bits_dev, void* st
 
 /* Workspace bytes apmoe_bitplane_lut_gemm needs for these shapes. */
 size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I);
+
+/* uint32 words of all six packed planes of a rows x cols matrix:
+ * 6 * rows * 4 * ceil(cols / 128). */
+size_t apmoe_packed_plane_words(int rows, int cols);
+
+/*
+ * Reorder canonical planes [6][rows][cols/32] into the packed layout the
+ * kernels read (a one-time weight preparation, not part of a layer call).
+ *  src  device, canonical planes;  dst  device, apmoe_packed_plane_words()
+ *  words, must not overlap src.  rows % 16 == 0 and cols % 32 == 0.
+ */
+int apmoe_pack_planes(const uint32_t* src, int rows, int cols, uint32_t* dst, void* stream);
 
 /* Static description of an error code. */
 const char* apmoe_strerror(int code);

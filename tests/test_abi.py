@@ -15,7 +15,7 @@ from oracle import planner as planner_ref
 def test_library_exports_header_symbols():
     lib = _lib._lib()
     names = _lib.header_symbols()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -58,6 +58,11 @@ def test_validation_before_launch():
     # combine
     assert lib.apmoe_combine(fake, fake, fake, 4, 2, 48, None, fake, None) == _lib.EINVAL
     assert lib.apmoe_combine(None, fake, fake, 4, 2, 64, None, fake, None) == _lib.EINVAL
+    # pack: rows not a multiple of 16, cols not a multiple of 32, overlap
+    assert lib.apmoe_pack_planes(fake, 24, 64, ctypes.c_void_p(0x100000), None) == _lib.EINVAL
+    assert lib.apmoe_pack_planes(fake, 32, 48, ctypes.c_void_p(0x100000), None) == _lib.EINVAL
+    assert lib.apmoe_pack_planes(fake, 32, 64, fake, None) == _lib.EINVAL
+    assert _lib.packed_plane_words(32, 704) == 6 * 32 * 4 * 6
     # commit: invalid bitwidth rejected on the host
     bad = (ctypes.c_int8 * 3)(6, 7, 3)
     assert lib.apmoe_commit_bits(bad, 3, fake, None) == _lib.EBITS

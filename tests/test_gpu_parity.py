@@ -38,7 +38,7 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("mfma_min", [ALL_GEMV, ALL_TILE, 16])
+@pytest.mark.parametrize("mfma_min", [ALL_GEMV, ALL_TILE, 16, 65])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layer_every_step(name, mfma_min):
     cfg = SMALL[name]
@@ -132,3 +132,22 @@ def test_full_size_layer(name):
         G.check_experts(inp, bits, got, experts=[touched[0], touched[-1]])
     G.say(f"  ambiguous routes {n_amb}, layer err/bound {ratio:.3g}, "
           f"groups {sorted(got['counts'].tolist(), reverse=True)[:8]}")
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 32), (32, 704), (48, 320), (64, 4096)])
+def test_pack_planes_layout(rows, cols):
+    """Packed word [p][group][step][g][i] is canonical word 4*step + g of row
+    16*group + i of plane p (zero past the last word)."""
+    import torch
+    rng = np.random.default_rng(rows * 7 + cols)
+    canon = rng.integers(0, 2**32, size=(6, rows, cols // 32), dtype=np.uint32)
+    src = torch.from_numpy(canon.view(np.int32)).cuda()
+    dst = torch.full((_lib.packed_plane_words(rows, cols),), -1, dtype=torch.int32, device="cuda")
+    _lib.pack_planes(src, rows, cols, dst)
+    got = dst.cpu().numpy().view(np.uint32)
+    W = cols // 32
+    ns = (W + 3) // 4
+    padded = np.zeros((6, rows, 4 * ns), dtype=np.uint32)
+    padded[:, :, :W] = canon
+    expect = padded.reshape(6, rows // 16, 16, ns, 4).transpose(0, 1, 3, 4, 2).reshape(-1)
+    assert np.array_equal(got, expect)
