@@ -14,6 +14,7 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t uint32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kPlanes = 6;

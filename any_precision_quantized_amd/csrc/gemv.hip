@@ -3,296 +3,196 @@
 //
 // Layout of the work (gfx950, wave64, v_mfma_f32_16x16x32_f16):
 //   D[row][token] = sum_k W[row][k] * X[token][k]
-//   A operand (W): lane l holds row (l % 16) of a 16-row group and the eight
-//                  consecutive columns 8*q + 0..7 of the 32-column word that
-//                  lane group g = l / 16 owns in this step (q = 0..3 picks
-//                  one of the four MFMAs a word feeds).
-//   B operand (X): lane l holds token (l % 16) at the same eight columns; one
-//                  16-byte load from the activation row.
+//   A operand (W): lane l holds row (l % 16) of the wave's 16-row block and
+//                  the eight consecutive columns 8*q + 0..7 of the 32-column
+//                  word that lane group g = l / 16 owns in this K step
+//                  (a step is 128 columns; q = 0..3 picks one of the four
+//                  MFMAs a word feeds).
+//   B operand (X): lane l holds token (l % 16) of a 16-token tile at the
+//                  same eight columns, read from LDS.
 //   D:             lane l holds rows 4*g + 0..3 for token l % 16.
-// A decoded A operand is reused for up to four 16-token tiles.
+// One decoded A operand feeds up to four 16-token tiles.
+//
+// A workgroup is four waves on four consecutive 16-row blocks of one expert
+// (one item: expert, 64-row block, K split), so the four waves read the same
+// activations: the workgroup stages each K step's activation tiles in LDS
+// once (double-buffered, one barrier per step) and every wave reads its B
+// operands from there.  The grid holds one workgroup per possible item and
+// is not persistent: the hardware dispatcher hands items to free CUs, which
+// balances items of very different cost (3..6-bit or fp16 rows, 1..4 tiles).
 //
 // Decode of one lane's word (32 columns of one row, b planes):
 //   * the plane words come from the packed layout: one 256-byte run per plane
-//     and 16-row group per step, so every load uses whole cache lines;
-//   * the b plane words are bit-transposed in registers with three delta-swap
-//     stages, giving eight registers R_s whose byte u is the b-bit code of
-//     column 8*u + s (one 8x8 bit transpose per byte lane);
-//   * each wave stages the LUTs of its rows in its own 16 KB LDS region as
-//     table[code][matrix][slot] dwords, slot = 16*(g % 2) + row, so the 32
-//     lanes of a half-wave read 32 different banks whatever the codes;
-//   * the region number rides in code bits 6-7 (two constant input words of
-//     the transpose), so a lookup address is code' * 256 + 4 * (lane % 32),
-//     built with one byte permute.
+//     and 16-row group per step, so every load uses whole cache lines, and
+//     they are issued two (down: four) steps ahead into a register ring;
+//   * the b plane words are bit-transposed in registers with delta swaps,
+//     giving eight registers R_s whose byte u is the b-bit code of column
+//     8*u + s (an 8x8 bit transpose per byte lane; the swaps of distance 1
+//     and 2 run first, while the planes past b are still zero words, so
+//     they cost nothing);
+//   * each wave stages the LUTs of its rows in LDS as table[code] rows of 256
+//     bytes shared by a pair of waves, the wave's 128-byte half holding 32
+//     dword slots, slot = 16*(g % 2) + row, so the 32 lanes of a half-wave read
+//     32 different banks whatever the codes; for gate/up the gate entry is the
+//     low and the up entry the high half of a slot.  A lookup address is
+//     pair * 64K + code * 256 + 128 * (wave % 2) + 4 * (lane % 32), built with
+//     one byte permute;
+//   * lookups return a weight in the low half of a dword; the even columns of
+//     a group feed one MFMA, the odd columns a second against activations
+//     shifted down one half, so no instruction packs pairs of halves.
 // Only the top b planes of a b-bit expert are read.
 //
-// Scheduling: a persistent grid walks a work list of items (expert, block of
-// 16 or 32 rows, K split) built on the device from the slot counts.  Each wave
-// owns whole items, so waves never wait for each other.  Loads are issued one
-// K step ahead into two register buffers that trade roles.  When the host
-// splits K (only when the work list would be too short to fill the GPU), each
-// split writes fp32 partial sums to the workspace and a finalize kernel adds
-// them in split order (and applies SwiGLU), so results never depend on
-// scheduling.
+// When the host splits K (only when the items of the possible experts would
+// leave CUs idle), each split writes fp32 partial sums to the workspace and a
+// finalize kernel adds them in split order (and applies SwiGLU), so results
+// never depend on scheduling.
 #include "common.hpp"
 
 namespace apmoe {
 namespace {
 
-constexpr int kWaves = 4;                   // waves per workgroup, one LDS region each
+constexpr int kWaves = 4;                    // 16-row blocks per item
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRegion = 16 * 1024;          // LUT bytes per wave: P * 2^b * 256 <= 16 KB
-constexpr int kTargetWaves = 2048;          // 256 CUs x 8 resident waves
+constexpr int kItemRows = 16 * kWaves;
+constexpr int kMaxTiles = 4;                 // 16-token tiles per pass
+constexpr int kXRow = 272;                   // bytes per token row of a tile (128 halves + 16 pad)
+constexpr int kXTile = 16 * kXRow;
+// LDS: LUT block of waves 0/1 at 0, activation ring at 16K, LUT block of
+// waves 2/3 at 64K (the permute puts the block index into address byte 2).
+constexpr int kLutBlock = 64 * 256;          // 2^6 codes x 256 bytes
+constexpr int kXRing = kLutBlock;
+constexpr int kLdsBytes = 65536 + kLutBlock;
+static_assert(kXRing + 2 * kMaxTiles * kXTile <= 65536, "activation ring overlaps the second LUT block");
+constexpr int kTargetGroups = 1024;          // 256 CUs x 2 resident workgroups, twice over
 
+// Exchange the bits of b selected by m with the bits of a selected by m << d.
 __device__ __forceinline__ void delta_swap(uint32_t& a, uint32_t& b, int d, uint32_t m) {
-    const uint32_t t = ((a >> d) ^ b) & m;
-    b ^= t;
-    a ^= t << d;
+    const uint32_t hi = m << d;
+    const uint32_t na = (a & ~hi) | ((b << d) & hi);
+    const uint32_t nb = (b & ~m) | ((a >> d) & m);
+    a = na;
+    b = nb;
 }
 
 // q[r] holds code bit r of 32 columns (bit i = column i).  Afterwards byte u of
-// q[s] holds the code of column 8*u + s.
+// q[s] holds the code of column 8*u + s.  The three stages commute; distance 1
+// and 2 go first so that the all-zero words past the top plane fold away.
 __device__ __forceinline__ void transpose_bytes(uint32_t q[8]) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) delta_swap(q[r], q[r + 4], 4, 0x0F0F0F0Fu);
+    for (int r = 0; r < 8; r += 2) delta_swap(q[r], q[r + 1], 1, 0x55555555u);
 #pragma unroll
     for (int r = 0; r < 8; r += 4) {
         delta_swap(q[r], q[r + 2], 2, 0x33333333u);
         delta_swap(q[r + 1], q[r + 3], 2, 0x33333333u);
     }
 #pragma unroll
-    for (int r = 0; r < 8; r += 2) delta_swap(q[r], q[r + 1], 1, 0x55555555u);
+    for (int r = 0; r < 4; ++r) delta_swap(q[r], q[r + 4], 4, 0x0F0F0F0Fu);
 }
 
-__device__ __forceinline__ half8_t load_h8(const half_t* p) { return *reinterpret_cast<const half8_t*>(p); }
-
-// Activations of eight columns, or zeros past the end of K (no branch).
-__device__ __forceinline__ half8_t load_x8(const half_t* p, bool ok) {
-    const half8_t v = load_h8(p);
-    const half8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
-    return ok ? v : z;
+// Raw buffer resources: 32-bit byte offsets from a uniform base, and loads
+// past num_records bytes return zero.
+constexpr int kBufFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufFlags);
 }
-
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+__device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ half8_t buf_load_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // any offset past num_records reads zeros
 
+// Weight sources of one item.  Buffer resources are rebuilt per load group
+// with num_records = 0 when the group is not needed, so every load is issued
+// unconditionally (static wait counts) and unneeded ones move no data.
 struct Mats {
-    gu32_t* planes[2];
-    gh16_t* lut[2];
-    gh16_t* w16[2];
+    gu32_t* lut[2];          // LUT_b as pairs of halves, [rows][2^b]
+    const void* planes[2];   // packed plane slabs
+    const void* w16[2];      // fp16 rows
+    uint32_t pbytes, wbytes;
 };
 
 struct Shape {
     int rows, K, Wd, nsteps, k, KS, S;
-    const half_t* in;
+    const void* in;       // activations
+    uint32_t in_bytes;
     const int32_t* slots;
-    float* partial;      // [KS][S][NMAT][rows] when KS > 1
+    float* partial;       // [KS][S][NMAT][rows] when KS > 1
 };
 
 struct Item {
-    int e, off, m, b, P, row0, ks;
+    int e, off, m, b, rb, ks;
 };
 
-// Rows per item: two 16-row groups for single-tile groups whose tables fit.
-__device__ __forceinline__ int rows_groups(int m, int b) { return (m <= 16 && (b <= 5 || b == 16)) ? 2 : 1; }
+// Item of workgroup `idx`: experts on this path each own ceil(rows / 64) row
+// blocks times KS splits, in expert order.  Every wave finds it on its own
+// (a wave-wide scan over the slot counts); returns false past the last item.
+__device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, int idx, Item& it) {
+    const int lane = threadIdx.x % kWave;
+    const int blk = idx / KS;
+    int base = 0;
+    for (int c0 = 0; c0 < a.E; c0 += kWave) {
+        const int e = c0 + lane;
+        int m = 0, b = 0;
+        if (e < a.E) {
+            m = a.offsets[e + 1] - a.offsets[e];
+            b = a.bits[e];
+        }
+        const int n = (m > 0 && m < a.mfma_min_tokens && valid_bits(b)) ? nrb : 0;
+        int inc = n;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int t = __shfl_up(inc, o, kWave);
+            if (lane >= o) inc += t;
+        }
+        const int first = base + inc - n;
+        const unsigned long long hit = __ballot(n > 0 && blk >= first && blk < first + n);
+        if (hit) {
+            const int src = __ffsll((long long)hit) - 1;
+            it.e = __builtin_amdgcn_readfirstlane(c0 + src);
+            it.m = __builtin_amdgcn_readfirstlane(__shfl(m, src, kWave));
+            it.b = __builtin_amdgcn_readfirstlane(__shfl(b, src, kWave));
+            it.rb = __builtin_amdgcn_readfirstlane(blk - __shfl(first, src, kWave));
+            it.off = a.offsets[it.e];
+            it.ks = idx % KS;
+            return true;
+        }
+        base += __shfl(inc, kWave - 1, kWave);
+    }
+    return false;
+}
 
-// Stage the LUTs of one item into this wave's region, at byte offset
-//   r * 2^B * 256 + v * 256 + mat * 128 + 4 * slot,  slot = 16 * c + row, c = 0, 1.
-template <int NMAT, int B, int P>
-__device__ __forceinline__ void stage_luts(uint32_t* region, const Mats& mv, int row0, int lane) {
+// Stage the LUTs of this wave's 16 rows: code v's 128-byte half row holds
+// the entry of row (slot % 16) in slots slot and slot + 16; gate in the low
+// and up in the high half of each dword.  Lanes cover 32 slots x 2 codes per
+// store, so each half-wave writes one whole half row (no bank conflicts).
+template <int NMAT, int B>
+__device__ __forceinline__ void stage_luts(char* tab, const Mats& mv, int rowc, int lane) {
     constexpr int nent = 1 << B;
-    constexpr int total = P * NMAT * nent * 16;
-    for (int idx = lane; idx < total; idx += kWave) {
-        const int v = idx % nent;                 // consecutive lanes: consecutive entries of one row
-        const int i = (idx / nent) & 15;
-        const int t = idx / (nent * 16);          // r * NMAT + mat
-        const int r = t / NMAT, mat = t % NMAT;
-        gh16_t* lut = (NMAT == 2 && mat) ? mv.lut[1] : mv.lut[0];
-        const uint32_t val = ((gu16_t*)lut)[(size_t)(row0 + 16 * r + i) * nent + v];
-        uint32_t* tab = region + (r * nent + v) * 64 + mat * 32 + i;
-        tab[0] = val;
-        tab[16] = val;
-    }
-}
-
-// Plane words of one K step for every (row group, matrix) of the item, from
-// the packed layout: one 256-byte run per plane and row group.
-template <int NMAT, int B, int P>
-__device__ __forceinline__ void load_planes(uint32_t (&w)[P][NMAT][B], const Mats& mv, const Shape& sh, int row0,
-                                            int step, int lane) {
-    const size_t slab = (size_t)sh.rows * 4 * sh.nsteps;
+    const int sl = lane & 31;
+    const int row = rowc + (sl & 15);
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
-        const size_t at = ((size_t)((row0 >> 4) + r) * sh.nsteps + step) * 64 + lane;
-#pragma unroll
-        for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-            for (int p = 0; p < B; ++p) w[r][mat][p] = mv.planes[mat][p * slab + at];
-    }
-}
-
-// Activations of one K step (four MFMA column groups x TT tiles).
-template <int TT>
-__device__ __forceinline__ void load_x(half8_t (&bx)[4][TT], const half_t* const (&xr)[TT], int word, int Wd) {
-    const bool ok = word < Wd;
-    const int wc = min(word, Wd - 1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) bx[q][tt] = load_x8(xr[tt] + 32 * wc + 8 * q, ok);
-}
-
-// Decode one step's plane words and run its MFMAs.  hi6/hi7 hold code bits 6
-// and 7 (the wave's LDS region) for every column: all ones or zero.
-template <int NMAT, int B, int P, int TT>
-__device__ __forceinline__ void lut_step(const uint32_t (&w)[P][NMAT][B], const half8_t (&bx)[4][TT],
-                                         const char* lds, uint32_t lane_off, uint32_t hi6, uint32_t hi7,
-                                         float4_t (&acc)[P][NMAT][TT]) {
-    uint32_t qv[P][NMAT][8];
-#pragma unroll
-    for (int r = 0; r < P; ++r)
-#pragma unroll
-        for (int mat = 0; mat < NMAT; ++mat) {
-#pragma unroll
-            for (int rr = 0; rr < 6; ++rr) qv[r][mat][rr] = rr < B ? w[r][mat][B - 1 - rr] : 0u;  // bit rr <- plane B-1-rr
-            qv[r][mat][6] = hi6;
-            qv[r][mat][7] = hi7;
-            transpose_bytes(qv[r][mat]);
+    for (int v0 = 0; v0 < nent; v0 += 4) {
+        const int v = v0 + 2 * (lane >> 5);
+        const uint32_t g = mv.lut[0][(row * nent + v) >> 1];
+        uint32_t e0 = g & 0xFFFFu, e1 = g >> 16;
+        if (NMAT == 2) {
+            const uint32_t u = mv.lut[1][(row * nent + v) >> 1];
+            e0 = __builtin_amdgcn_perm(u, g, 0x05040100u);
+            e1 = __builtin_amdgcn_perm(u, g, 0x07060302u);
         }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        // address = (region << 6 | code) * 256 + 4 * (lane % 32), code = byte q of R_s
-        const uint32_t sel = 0x0C0C0000u | ((4u + q) << 8);
-#pragma unroll
-        for (int r = 0; r < P; ++r)
-#pragma unroll
-            for (int mat = 0; mat < NMAT; ++mat) {
-                const char* tab = lds + r * (1 << B) * 256 + mat * 128;
-                half8_t a;
-#pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    a[s] = *reinterpret_cast<const half_t*>(tab + __builtin_amdgcn_perm(qv[r][mat][s], lane_off, sel));
-#pragma unroll
-                for (int tt = 0; tt < TT; ++tt)
-                    acc[r][mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bx[q][tt], acc[r][mat][tt], 0, 0, 0);
-            }
+        *reinterpret_cast<uint32_t*>(tab + v * 256 + 4 * sl) = e0;
+        *reinterpret_cast<uint32_t*>(tab + (v + 1) * 256 + 4 * sl) = e1;
     }
 }
 
-// K loop of one wave over steps [s0, s1): in each step lane group g owns word
-// 4*step + g of every (row group, matrix) of the item.  Everything a step needs
-// is issued one step ahead, before the loads of the step after it, so the
-// in-order completion of loads never makes a step wait for its successor's
-// data; two register buffers trade roles (unrolled by two) so no register is
-// copied while its load is in flight.
-template <int NMAT, int B, int P, int TT>
-__device__ __forceinline__ void kloop(const Mats& mv, const char* lds, const Shape& sh, const Item& it, int t0,
-                                      int s0, int s1, int lane, uint32_t hi6, uint32_t hi7,
-                                      float4_t (&acc)[P][NMAT][TT]) {
-    const int i = lane & 15, g = lane >> 4;
-    const half_t* xr[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-        const int n = min(t0 + 16 * tt + i, it.m - 1);
-        xr[tt] = NMAT == 2 ? sh.in + (size_t)(sh.slots[it.off + n] / sh.k) * sh.K
-                           : sh.in + (size_t)(it.off + n) * sh.K;
-    }
-    if (s0 >= s1) return;
-    const int last = 4 * (s1 - 1) + g;   // past the last step: re-read it (from cache)
-    half8_t xa[4][TT], xb[4][TT == 1 ? 1 : 1];
-    if constexpr (B == 16) {
-        half8_t wa[P][NMAT][4], wb[P][NMAT][4];
-        auto load_w = [&](half8_t (&w)[P][NMAT][4], int word) {
-            const int wc = min(word, sh.Wd - 1);
-#pragma unroll
-            for (int r = 0; r < P; ++r)
-#pragma unroll
-                for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        w[r][mat][q] = load_h8g(mv.w16[mat] + (size_t)(it.row0 + 16 * r + i) * sh.K + 32 * wc + 8 * q);
-        };
-        auto mma = [&](const half8_t (&w)[P][NMAT][4], const half8_t (&bx)[4][TT]) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int r = 0; r < P; ++r)
-#pragma unroll
-                    for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-                        for (int tt = 0; tt < TT; ++tt)
-                            acc[r][mat][tt] =
-                                __builtin_amdgcn_mfma_f32_16x16x32_f16(w[r][mat][q], bx[q][tt], acc[r][mat][tt], 0, 0, 0);
-        };
-        if constexpr (TT == 1) {
-            load_x<TT>(xa, xr, 4 * s0 + g, sh.Wd);
-            load_w(wa, 4 * s0 + g);
-            for (int step = s0; step < s1; step += 2) {
-                const int w1 = min(4 * (step + 1) + g, last), w2 = min(4 * (step + 2) + g, last);
-                load_x<TT>(xb, xr, w1, sh.Wd);
-                load_w(wb, w1);
-                mma(wa, xa);
-                load_x<TT>(xa, xr, w2, sh.Wd);
-                load_w(wa, w2);
-                if (step + 1 < s1) mma(wb, xb);
-            }
-        } else {
-            // multi-tile activations take one buffer, loaded at the start of
-            // each step ahead of the next step's weights
-            load_w(wa, 4 * s0 + g);
-            for (int step = s0; step < s1; step += 2) {
-                const int w0 = 4 * step + g;
-                const int w1 = min(4 * (step + 1) + g, last), w2 = min(4 * (step + 2) + g, last);
-                load_x<TT>(xa, xr, w0, sh.Wd);
-                load_w(wb, w1);
-                mma(wa, xa);
-                load_x<TT>(xa, xr, w1, sh.Wd);
-                load_w(wa, w2);
-                if (step + 1 < s1) mma(wb, xa);
-            }
-        }
-    } else {
-        const uint32_t lane_off = 4u * (lane & 31);
-        uint32_t wa[P][NMAT][B], wb[P][NMAT][B];
-        const int sl = s1 - 1;   // past the last step: re-read it (from cache)
-        if constexpr (TT == 1) {
-            load_x<TT>(xa, xr, 4 * s0 + g, sh.Wd);
-            load_planes<NMAT, B, P>(wa, mv, sh, it.row0, s0, lane);
-            for (int step = s0; step < s1; step += 2) {
-                const int w1 = min(4 * (step + 1) + g, last), w2 = min(4 * (step + 2) + g, last);
-                load_x<TT>(xb, xr, w1, sh.Wd);
-                load_planes<NMAT, B, P>(wb, mv, sh, it.row0, min(step + 1, sl), lane);
-                lut_step<NMAT, B, P, TT>(wa, xa, lds, lane_off, hi6, hi7, acc);
-                load_x<TT>(xa, xr, w2, sh.Wd);
-                load_planes<NMAT, B, P>(wa, mv, sh, it.row0, min(step + 2, sl), lane);
-                if (step + 1 < s1) lut_step<NMAT, B, P, TT>(wb, xb, lds, lane_off, hi6, hi7, acc);
-            }
-        } else {
-            load_planes<NMAT, B, P>(wa, mv, sh, it.row0, s0, lane);
-            for (int step = s0; step < s1; step += 2) {
-                const int w0 = 4 * step + g;
-                const int w1 = min(4 * (step + 1) + g, last);
-                load_x<TT>(xa, xr, w0, sh.Wd);
-                load_planes<NMAT, B, P>(wb, mv, sh, it.row0, min(step + 1, sl), lane);
-                lut_step<NMAT, B, P, TT>(wa, xa, lds, lane_off, hi6, hi7, acc);
-                load_x<TT>(xa, xr, w1, sh.Wd);
-                load_planes<NMAT, B, P>(wa, mv, sh, it.row0, min(step + 2, sl), lane);
-                if (step + 1 < s1) lut_step<NMAT, B, P, TT>(wb, xa, lds, lane_off, hi6, hi7, acc);
-            }
-        }
-    }
-}
-
-// Results of row group r, token tok in this lane (rows 4g..4g+3): the final
-// value, or this K split's partial sums.
+// Results of one 16-token tile in this lane (rows row..row+3, token tok): the
+// final value, or this K split's partial sums.
 template <int NMAT>
-__device__ __forceinline__ void store_result(const GemmArgs& a, const Shape& sh, const Item& it, int r, int tok,
-                                             int g, const float4_t (&s)[NMAT]) {
+__device__ __forceinline__ void store_result(const GemmArgs& a, const Shape& sh, const Item& it, int row, int tok,
+                                             const float4_t (&s)[NMAT]) {
     if (tok >= it.m) return;
-    const int row = it.row0 + 16 * r + 4 * g;
     const int p = it.off + tok;
     if (sh.KS > 1) {
         float* dst = sh.partial + ((size_t)it.ks * sh.S + p) * NMAT * sh.rows + row;
@@ -311,96 +211,211 @@ __device__ __forceinline__ void store_result(const GemmArgs& a, const Shape& sh,
     }
 }
 
-// One item on one wave: stage its LUTs in the wave's region, then one pass
-// over its K range per 16*TT tokens.
-template <int NMAT, int B, int P, int TT>
-__device__ __forceinline__ void run_item(const GemmArgs& a, const Mats& mv, const char* lds, char* region,
-                                         const Shape& sh, const Item& it, int lane, uint32_t hi6, uint32_t hi7) {
+// One pass of the workgroup over its K steps [s0, s1) for the tokens
+// t0 .. t0 + 16*TT - 1 of the item.  Per step: issue the next step's
+// activation loads and the weight loads D steps ahead, run this step's MFMAs
+// (B operands from the LDS tile), write the next activation tile, barrier.
+template <int NMAT, int B, int TT>
+__device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape& sh, const Item& it, const Mats& mv,
+                                      int t0, int s0, int s1, int wave, int lane, bool live, int rowc) {
+    constexpr int D = (NMAT == 2) ? 2 : 4;   // steps of weights in flight
+    constexpr int NB = D + 1;
+    const int tid = threadIdx.x;
     const int i = lane & 15, g = lane >> 4;
-    const int per = (sh.nsteps + sh.KS - 1) / sh.KS;
-    const int s0 = min(sh.nsteps, it.ks * per), s1 = min(sh.nsteps, s0 + per);
-    if (B != 16) {
-        wave_lds_fence();   // the previous item's lookups come before the tables change
-        stage_luts<NMAT, B, P>(reinterpret_cast<uint32_t*>(region), mv, it.row0, lane);
-        wave_lds_fence();
+
+    // activation staging: thread -> token row xn of every tile, 16-byte chunk xc
+    const int xc = tid & 15, xn = tid >> 4;
+    uint32_t xrow[TT];
+    bool xok[TT];
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+        const int n = t0 + 16 * j + xn;
+        xok[j] = n < it.m;
+        const int nn = min(n, it.m - 1);
+        const int row = NMAT == 2 ? sh.slots[it.off + nn] / sh.k : it.off + nn;
+        xrow[j] = (uint32_t)row * (uint32_t)sh.K * 2u;
     }
-    for (int t0 = 0; t0 < it.m; t0 += 16 * TT) {
-        float4_t acc[P][NMAT][TT];
+    char* ring = lds + kXRing;
+    half8_t xs[TT];
+    auto x_load = [&](int s) {   // steps past s1 read zeros
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(sh.in, s < s1 ? sh.in_bytes : 0u);
+        const int col = 128 * s + 8 * xc;
 #pragma unroll
-        for (int r = 0; r < P; ++r)
+        for (int j = 0; j < TT; ++j)
+            xs[j] = buf_load_h8(r, (xok[j] && col < sh.K) ? xrow[j] + 2u * (uint32_t)col : kOutOfRange);
+    };
+    auto x_store = [&](int slot) {
+        char* p = ring + slot * (TT * kXTile) + xn * kXRow + 16 * xc;
 #pragma unroll
-            for (int mat = 0; mat < NMAT; ++mat)
+        for (int j = 0; j < TT; ++j) *reinterpret_cast<half8_t*>(p + j * kXTile) = xs[j];
+    };
+
+    float4_t acc[NMAT][TT];
 #pragma unroll
-                for (int tt = 0; tt < TT; ++tt) acc[r][mat][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
-        kloop<NMAT, B, P, TT>(mv, lds, sh, it, t0, s0, s1, lane, hi6, hi7, acc);
+    for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-        for (int r = 0; r < P; ++r)
+        for (int tt = 0; tt < TT; ++tt) acc[mat][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // B operands of column group q from a ring slot, and their odd halves
+    auto b_ops = [&](int slot, int q, half8_t (&bx)[TT], half8_t (&bo)[TT]) {
+        const char* p = ring + slot * (TT * kXTile) + i * kXRow + 64 * g + 16 * q;
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                float4_t s[NMAT];
+        for (int tt = 0; tt < TT; ++tt) {
+            bx[tt] = *reinterpret_cast<const half8_t*>(p + tt * kXTile);
+            uint32x4_t u = __builtin_bit_cast(uint32x4_t, bx[tt]);
 #pragma unroll
-                for (int mat = 0; mat < NMAT; ++mat) s[mat] = acc[r][mat][tt];
-                store_result<NMAT>(a, sh, it, r, t0 + 16 * tt + i, g, s);
+            for (int c = 0; c < 4; ++c) u[c] >>= 16;
+            bo[tt] = __builtin_bit_cast(half8_t, u);
+        }
+    };
+
+    if constexpr (B == 16) {
+        half8_t wr[NB][NMAT][4];
+        auto w_load = [&](half8_t (&w)[NMAT][4], int s) {   // idle waves and steps past s1 read zeros
+            const uint32_t n = (live && s < s1) ? mv.wbytes : 0u;
+            const int word = 4 * s + g;
+            const uint32_t base = ((uint32_t)(rowc + i) * (uint32_t)sh.K + 32u * word) * 2u;
+#pragma unroll
+            for (int mat = 0; mat < NMAT; ++mat) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(mv.w16[mat], n);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[mat][q] = buf_load_h8(r, word < sh.Wd ? base + 16u * q : kOutOfRange);
             }
+        };
+        auto compute = [&](const half8_t (&w)[NMAT][4], int slot) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                half8_t bx[TT], bo[TT];
+                b_ops(slot, q, bx, bo);
+#pragma unroll
+                for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt)
+                        acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[mat][q], bx[tt], acc[mat][tt], 0, 0, 0);
+            }
+        };
+        x_load(s0);
+#pragma unroll
+        for (int u = 0; u < D; ++u) w_load(wr[u], s0 + u);
+        x_store(0);
+        __syncthreads();
+        for (int s = s0; s < s1; s += NB) {
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int st = s + u;   // past s1 (the last group's tail): loads read zeros, no MFMAs
+                x_load(st + 1);
+                w_load(wr[(u + D) % NB], st + D);
+                if (live && st < s1) compute(wr[u], (st - s0) & 1);
+                x_store((st + 1 - s0) & 1);
+                __syncthreads();
+            }
+        }
+    } else {
+        uint32_t pw[NB][NMAT][B];
+        const uint32_t slab = (uint32_t)sh.rows * 16u * (uint32_t)sh.nsteps;   // bytes per plane
+        const uint32_t rg = (uint32_t)(rowc >> 4);
+        auto p_load = [&](uint32_t (&w)[NMAT][B], int s) {   // idle waves and steps past s1 read zeros
+            const uint32_t n = (live && s < s1) ? mv.pbytes : 0u;
+            const uint32_t at = (rg * (uint32_t)sh.nsteps + (uint32_t)min(s, sh.nsteps - 1)) * 256u + 4u * lane;
+#pragma unroll
+            for (int mat = 0; mat < NMAT; ++mat) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(mv.planes[mat], n);
+#pragma unroll
+                for (int p = 0; p < B; ++p) w[mat][p] = buf_load_u32(r, p * slab + at);
+            }
+        };
+        // lookup address: byte 0 = lane slot offset, byte 1 = code, byte 2 = LUT block
+        const uint32_t lane_off = ((uint32_t)(wave >> 1) << 16) | ((uint32_t)(wave & 1) << 7) | (4u * (lane & 31));
+        auto compute = [&](const uint32_t (&w)[NMAT][B], int slot) {
+            uint32_t qv[NMAT][8];
+#pragma unroll
+            for (int mat = 0; mat < NMAT; ++mat) {
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr) qv[mat][rr] = rr < B ? w[mat][B - 1 - rr] : 0u;  // bit rr <- plane B-1-rr
+                transpose_bytes(qv[mat]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                half8_t bx[TT], bo[TT];
+                b_ops(slot, q, bx, bo);
+                const uint32_t sel = 0x0C020400u | ((uint32_t)q << 8);
+#pragma unroll
+                for (int mat = 0; mat < NMAT; ++mat) {
+                    uint32x4_t ev, od;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        ev[c] = *reinterpret_cast<const uint16_t*>(lds + 2 * mat +
+                                                                   __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
+                        od[c] = *reinterpret_cast<const uint16_t*>(lds + 2 * mat +
+                                                                   __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
+                    }
+                    const half8_t ae = __builtin_bit_cast(half8_t, ev), ao = __builtin_bit_cast(half8_t, od);
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt) {
+                        acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bx[tt], acc[mat][tt], 0, 0, 0);
+                        acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo[tt], acc[mat][tt], 0, 0, 0);
+                    }
+                }
+            }
+        };
+        x_load(s0);
+#pragma unroll
+        for (int u = 0; u < D; ++u) p_load(pw[u], s0 + u);
+        x_store(0);
+        __syncthreads();   // also publishes the LUT tables
+        for (int s = s0; s < s1; s += NB) {
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int st = s + u;   // past s1 (the last group's tail): loads read zeros, no MFMAs
+                x_load(st + 1);
+                p_load(pw[(u + D) % NB], st + D);
+                if (live && st < s1) compute(pw[u], (st - s0) & 1);
+                x_store((st + 1 - s0) & 1);
+                __syncthreads();
+            }
+        }
+    }
+
+    if (live) {
+        const int row = rowc + 4 * g;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            float4_t s[NMAT];
+#pragma unroll
+            for (int mat = 0; mat < NMAT; ++mat) s[mat] = acc[mat][tt];
+            store_result<NMAT>(a, sh, it, row, t0 + 16 * tt + i, s);
+        }
     }
 }
 
 template <int NMAT, int B>
-__device__ __forceinline__ void run_item_b(const GemmArgs& a, const Mats& mv, const char* lds, char* region,
-                                           const Shape& sh, const Item& it, int lane, uint32_t hi6, uint32_t hi7) {
-    if (it.P == 2) {
-        run_item<NMAT, B, 2, 1>(a, mv, lds, region, sh, it, lane, hi6, hi7);
-    } else if (it.m <= 16) {
-        run_item<NMAT, B, 1, 1>(a, mv, lds, region, sh, it, lane, hi6, hi7);
-    } else if (it.m <= 32) {
-        run_item<NMAT, B, 1, 2>(a, mv, lds, region, sh, it, lane, hi6, hi7);
-    } else {
-        run_item<NMAT, B, 1, 4>(a, mv, lds, region, sh, it, lane, hi6, hi7);
+__device__ __forceinline__ void run_item(const GemmArgs& a, char* lds, const Shape& sh, const Item& it, const Mats& mv,
+                                         int wave, int lane) {
+    const int row0 = it.rb * kItemRows + 16 * wave;
+    const bool live = row0 < sh.rows;              // blocks past the last row idle but share the barriers
+    const int rowc = live ? row0 : sh.rows - 16;
+    const int per = (sh.nsteps + sh.KS - 1) / sh.KS;
+    const int s0 = min(sh.nsteps, it.ks * per), s1 = min(sh.nsteps, s0 + per);
+    if (s0 >= s1) return;   // uniform over the workgroup
+    if constexpr (B != 16) {
+        if (live) stage_luts<NMAT, B>(lds + (wave >> 1) * 65536 + (wave & 1) * 128, mv, rowc, lane);
     }
-}
-
-// Row blocks of the experts on this path, in expert order (identical in every
-// workgroup).
-struct WorkList {
-    int first[APMOE_MAX_EXPERTS + 1];
-    int nrb[APMOE_MAX_EXPERTS];
-    int cnt[APMOE_MAX_EXPERTS];
-};
-
-__device__ __forceinline__ void build_work_list(WorkList& wl, const GemmArgs& a, int rows) {
-    for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
-        const int m = a.offsets[e + 1] - a.offsets[e];
-        const int b = a.bits[e];
-        const bool on = m > 0 && m < a.mfma_min_tokens && valid_bits(b);
-        wl.cnt[e] = m;
-        wl.nrb[e] = on ? rows / (16 * rows_groups(m, b)) : 0;
+    for (int t0 = 0; t0 < it.m; t0 += 16 * kMaxTiles) {
+        const int left = it.m - t0;
+        if (left > 32)
+            kpass<NMAT, B, 4>(a, lds, sh, it, mv, t0, s0, s1, wave, lane, live, rowc);
+        else if (left > 16)
+            kpass<NMAT, B, 2>(a, lds, sh, it, mv, t0, s0, s1, wave, lane, live, rowc);
+        else
+            kpass<NMAT, B, 1>(a, lds, sh, it, mv, t0, s0, s1, wave, lane, live, rowc);
+        if (t0 + 16 * kMaxTiles < it.m) __syncthreads();   // the ring is reused by the next pass
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int e = 0; e < a.E; ++e) {
-            wl.first[e] = run;
-            run += wl.nrb[e];
-        }
-        wl.first[a.E] = run;
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ int expert_of(const WorkList& wl, int E, int blk) {
-    int lo = 0, hi = E - 1;   // last e with first[e] <= blk
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (wl.first[mid] <= blk) lo = mid; else hi = mid - 1;
-    }
-    return lo;
 }
 
 template <int NMAT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemv_kernel(GemmArgs a, int KS, float* partial) {
-    __shared__ __attribute__((aligned(16))) char lds[kWaves * kRegion];
-    __shared__ WorkList wl;
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
     Shape sh;
     sh.rows = NMAT == 2 ? a.I : a.H;
@@ -410,50 +425,36 @@ void gemv_kernel(GemmArgs a, int KS, float* partial) {
     sh.k = a.k;
     sh.KS = KS;
     sh.S = a.T * a.k;
-    sh.in = reinterpret_cast<const half_t*>(a.in);
     sh.slots = a.sorted_slots;
     sh.partial = partial;
+    sh.in = a.in;
+    sh.in_bytes = (uint32_t)((NMAT == 2 ? (size_t)a.T : (size_t)sh.S) * sh.K * 2);
 
-    build_work_list(wl, a, sh.rows);
-    const int total = wl.first[a.E] * KS;
+    Item it;
+    if (!find_item(a, (sh.rows + kItemRows - 1) / kItemRows, KS, blockIdx.x, it)) return;   // uniform
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
-    char* region = lds + wave * kRegion;                 // staging target of this wave
-    const uint32_t hi6 = (wave & 1) ? 0xFFFFFFFFu : 0u;  // lookups reach the region
-    const uint32_t hi7 = (wave & 2) ? 0xFFFFFFFFu : 0u;  // through code bits 6 and 7
 
-    const int nwaves = gridDim.x * kWaves;
-    for (int idx = blockIdx.x * kWaves + wave; idx < total; idx += nwaves) {
-        const int blk = idx / KS;
-        const int e = expert_of(wl, a.E, blk);
-        Item it;
-        it.e = e;
-        it.off = a.offsets[e];
-        it.m = wl.cnt[e];
-        it.b = a.bits[e];
-        it.P = rows_groups(it.m, it.b);
-        it.row0 = (blk - wl.first[e]) * 16 * it.P;
-        it.ks = idx % KS;
+    Mats mv;
+    const apmoe_mat& m0 = NMAT == 2 ? a.experts[it.e].gate : a.experts[it.e].down;
+    const apmoe_mat& m1 = a.experts[it.e].up;
+    const MatView v0 = mat_view(m0, it.b), v1 = mat_view(m1, it.b);
+    mv.lut[0] = (gu32_t*)v0.lut;
+    mv.lut[1] = (gu32_t*)v1.lut;
+    mv.planes[0] = (const void*)v0.planes;
+    mv.planes[1] = (const void*)v1.planes;
+    mv.w16[0] = (const void*)v0.w16;
+    mv.w16[1] = (const void*)v1.w16;
+    mv.pbytes = 6u * (uint32_t)sh.rows * 16u * (uint32_t)sh.nsteps;
+    mv.wbytes = (uint32_t)sh.rows * (uint32_t)sh.K * 2u;
 
-        Mats mv;
-        const apmoe_mat& m0 = NMAT == 2 ? a.experts[e].gate : a.experts[e].down;
-        const apmoe_mat& m1 = a.experts[e].up;
-        const MatView v0 = mat_view(m0, it.b), v1 = mat_view(m1, it.b);
-        mv.planes[0] = v0.planes;
-        mv.lut[0] = v0.lut;
-        mv.w16[0] = v0.w16;
-        mv.planes[1] = v1.planes;
-        mv.lut[1] = v1.lut;
-        mv.w16[1] = v1.w16;
-
-        switch (it.b) {
-            case 3: run_item_b<NMAT, 3>(a, mv, lds, region, sh, it, lane, hi6, hi7); break;
-            case 4: run_item_b<NMAT, 4>(a, mv, lds, region, sh, it, lane, hi6, hi7); break;
-            case 5: run_item_b<NMAT, 5>(a, mv, lds, region, sh, it, lane, hi6, hi7); break;
-            case 6: run_item_b<NMAT, 6>(a, mv, lds, region, sh, it, lane, hi6, hi7); break;
-            default: run_item_b<NMAT, 16>(a, mv, lds, region, sh, it, lane, hi6, hi7); break;
-        }
+    switch (it.b) {
+        case 3: run_item<NMAT, 3>(a, lds, sh, it, mv, wave, lane); break;
+        case 4: run_item<NMAT, 4>(a, lds, sh, it, mv, wave, lane); break;
+        case 5: run_item<NMAT, 5>(a, lds, sh, it, mv, wave, lane); break;
+        case 6: run_item<NMAT, 6>(a, lds, sh, it, mv, wave, lane); break;
+        default: run_item<NMAT, 16>(a, lds, sh, it, mv, wave, lane); break;
     }
 }
 
@@ -497,16 +498,21 @@ __global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, 
     }
 }
 
-}  // namespace
-
-// K splits, chosen from shapes alone: only when one item per row block of every
-// expert that could be active would leave waves idle (at least 4 K steps each).
-int gemv_splits(int T, int k, int E, int rows, int K) {
+long long items_per_split(int T, int k, int E, int rows) {
     const long long slots = (long long)T * k;
     const long long active = E < slots ? E : slots;
-    const long long items = active * (rows / 16);
+    return active * ((rows + kItemRows - 1) / kItemRows);
+}
+
+}  // namespace
+
+// K splits, chosen from shapes alone: only when one item per 64-row block of
+// every expert that could be active would leave CUs idle (at least 4 K steps
+// per split).
+int gemv_splits(int T, int k, int E, int rows, int K) {
+    const long long items = items_per_split(T, k, E, rows);
     const int nsteps = (K / 32 + 3) / 4;
-    long long ks = items > 0 ? (kTargetWaves + items - 1) / items : 1;
+    long long ks = items > 0 ? (kTargetGroups + items - 1) / items : 1;
     const int cap = nsteps / 4 > 1 ? nsteps / 4 : 1;
     if (ks > cap) ks = cap;
     return ks < 1 ? 1 : (int)ks;
@@ -529,7 +535,9 @@ int launch_gemv(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
         if (!ws || ws_bytes < gemv_workspace_bytes(a.T, a.k, a.E, rows, K, nmat)) return APMOE_ENOSPACE;
         partial = reinterpret_cast<float*>(ws);
     }
-    dim3 grid(kTargetWaves / kWaves), block(kThreads);
+    const long long groups = items_per_split(a.T, a.k, a.E, rows) * KS;
+    if (groups <= 0) return APMOE_OK;
+    dim3 grid((unsigned)groups), block(kThreads);
     if (gu)
         hipLaunchKernelGGL(gemv_kernel<2>, grid, block, 0, s, a, KS, partial);
     else
