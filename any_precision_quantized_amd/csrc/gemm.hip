@@ -24,6 +24,18 @@ __global__ __launch_bounds__(256) void tile_simple_kernel(GemmArgs a) {
     const int W = K / 32;
     const int n0 = blockIdx.x * kBN;
 
+    // Nothing to do unless some group reaches the threshold: one wave-wide
+    // vote per 64 experts, before any LDS traffic (uniform over the workgroup).
+    {
+        const int lane = threadIdx.x % kWave;
+        bool any = false;
+        for (int c0 = 0; c0 < a.E && !any; c0 += kWave) {
+            const int e = c0 + lane;
+            const int c = e < a.E ? a.offsets[e + 1] - a.offsets[e] : 0;
+            any = __ballot(c >= a.mfma_min_tokens) != 0;
+        }
+        if (!any) return;
+    }
     // Map blockIdx.y to (expert, m-tile) over the groups that take this path
     // (slot counts staged in LDS once, then a scan from LDS).
     __shared__ int cnt[APMOE_MAX_EXPERTS + 1];

@@ -24,7 +24,7 @@
 // Decode of one lane's word (32 columns of one row, b planes):
 //   * the plane words come from the packed layout: one 256-byte run per plane
 //     and 16-row group per step, so every load uses whole cache lines, and
-//     they are issued two (down: four) steps ahead into a register ring;
+//     they are issued three steps ahead into a register ring;
 //   * the b plane words are bit-transposed in registers with delta swaps,
 //     giving eight registers R_s whose byte u is the b-bit code of column
 //     8*u + s (an 8x8 bit transpose per byte lane; the swaps of distance 1
@@ -65,28 +65,52 @@ constexpr int kLdsBytes = 65536 + kLutBlock;
 static_assert(kXRing + 2 * kMaxTiles * kXTile <= 65536, "activation ring overlaps the second LUT block");
 constexpr int kTargetGroups = 1024;          // 256 CUs x 2 resident workgroups, twice over
 
-// Exchange the bits of b selected by m with the bits of a selected by m << d.
-__device__ __forceinline__ void delta_swap(uint32_t& a, uint32_t& b, int d, uint32_t m) {
-    const uint32_t hi = m << d;
-    const uint32_t na = (a & ~hi) | ((b << d) & hi);
-    const uint32_t nb = (b & ~m) | ((a >> d) & m);
-    a = na;
-    b = nb;
+// (x & m) | (y & ~m).  Written as the instruction itself: the compiler
+// otherwise re-canonicalises chains of these merges into longer sequences.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t x, uint32_t y) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(x), "v"(y));
+    return r;
 }
 
-// q[r] holds code bit r of 32 columns (bit i = column i).  Afterwards byte u of
-// q[s] holds the code of column 8*u + s.  The three stages commute; distance 1
-// and 2 go first so that the all-zero words past the top plane fold away.
-__device__ __forceinline__ void transpose_bytes(uint32_t q[8]) {
+// One delta-swap stage of distance D over rows r and r + D (r with bit D
+// clear): the bits of row r + D selected by m trade places with the bits of
+// row r selected by m << D.  NZ marks the rows that may be non-zero, so rows
+// known to be zero cost nothing (a lone non-zero row splits in two ops or
+// three).
+template <int D, int NZ>
+__device__ __forceinline__ void swap_stage(uint32_t q[8], uint32_t m) {
 #pragma unroll
-    for (int r = 0; r < 8; r += 2) delta_swap(q[r], q[r + 1], 1, 0x55555555u);
-#pragma unroll
-    for (int r = 0; r < 8; r += 4) {
-        delta_swap(q[r], q[r + 2], 2, 0x33333333u);
-        delta_swap(q[r + 1], q[r + 3], 2, 0x33333333u);
+    for (int r = 0; r < 8; ++r) {
+        if (r & D) continue;
+        const bool za = !((NZ >> r) & 1), zb = !((NZ >> (r + D)) & 1);
+        if (za && zb) continue;
+        const uint32_t hi = m << D;
+        if (zb) {
+            q[r + D] = (q[r] >> D) & m;
+            q[r] &= ~hi;
+        } else if (za) {
+            q[r] = (q[r + D] << D) & hi;
+            q[r + D] &= m;
+        } else {
+            const uint32_t a = q[r], b = q[r + D];
+            q[r] = bfi(hi, b << D, a);
+            q[r + D] = bfi(m, a >> D, b);
+        }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) delta_swap(q[r], q[r + 4], 4, 0x0F0F0F0Fu);
+}
+
+// q[r] holds code bit r of 32 columns (bit i = column i), rows r >= B zero.
+// Afterwards byte u of q[s] holds the code of column 8*u + s.  The three
+// stages commute; distance 1 and 2 go first, while rows B..7 are still zero.
+template <int B>
+__device__ __forceinline__ void transpose_bytes(uint32_t q[8]) {
+    constexpr int z0 = (1 << B) - 1;
+    constexpr int z1 = z0 | ((z0 & 0x55) << 1) | ((z0 & 0xAA) >> 1);
+    constexpr int z2 = z1 | ((z1 & 0x33) << 2) | ((z1 & 0xCC) >> 2);
+    swap_stage<1, z0>(q, 0x55555555u);
+    swap_stage<2, z1>(q, 0x33333333u);
+    swap_stage<4, z2>(q, 0x0F0F0F0Fu);
 }
 
 // Raw buffer resources: 32-bit byte offsets from a uniform base, and loads
@@ -95,8 +119,8 @@ constexpr int kBufFlags = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufFlags);
 }
-__device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+__device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, (int)soff, 0);
 }
 __device__ __forceinline__ half8_t buf_load_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -212,14 +236,16 @@ __device__ __forceinline__ void store_result(const GemmArgs& a, const Shape& sh,
 }
 
 // One pass of the workgroup over its K steps [s0, s1) for the tokens
-// t0 .. t0 + 16*TT - 1 of the item.  Per step: issue the next step's
-// activation loads and the weight loads D steps ahead, run this step's MFMAs
-// (B operands from the LDS tile), write the next activation tile, barrier.
+// t0 .. t0 + 16*TT - 1 of the item.  Per step: issue the activation loads two
+// steps ahead and the weight loads D steps ahead, run this step's MFMAs
+// (B operands from the LDS tile), write the next step's activation tile
+// (loaded a step earlier), barrier.
 template <int NMAT, int B, int TT>
 __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape& sh, const Item& it, const Mats& mv,
                                       int t0, int s0, int s1, int wave, int lane, bool live, int rowc) {
-    constexpr int D = (NMAT == 2) ? 2 : 4;   // steps of weights in flight
-    constexpr int NB = D + 1;
+    constexpr int D = 3;        // steps of weights in flight
+    constexpr int NB = D + 1;   // unroll: register ring of weights; even, so the
+                                // two activation buffers alternate with u
     const int tid = threadIdx.x;
     const int i = lane & 15, g = lane >> 4;
 
@@ -236,18 +262,20 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
         xrow[j] = (uint32_t)row * (uint32_t)sh.K * 2u;
     }
     char* ring = lds + kXRing;
-    half8_t xs[TT];
-    auto x_load = [&](int s) {   // steps past s1 read zeros
+    // activations travel global -> registers (two steps ahead) -> LDS ring
+    // slot (one step ahead); xs[k] holds the step with (step - s0) % 2 == k
+    half8_t xs[2][TT];
+    auto x_load = [&](half8_t (&x)[TT], int s) {   // steps past s1 read zeros
         const __amdgpu_buffer_rsrc_t r = make_rsrc(sh.in, s < s1 ? sh.in_bytes : 0u);
         const int col = 128 * s + 8 * xc;
 #pragma unroll
         for (int j = 0; j < TT; ++j)
-            xs[j] = buf_load_h8(r, (xok[j] && col < sh.K) ? xrow[j] + 2u * (uint32_t)col : kOutOfRange);
+            x[j] = buf_load_h8(r, (xok[j] && col < sh.K) ? xrow[j] + 2u * (uint32_t)col : kOutOfRange);
     };
-    auto x_store = [&](int slot) {
+    auto x_store = [&](const half8_t (&x)[TT], int slot) {
         char* p = ring + slot * (TT * kXTile) + xn * kXRow + 16 * xc;
 #pragma unroll
-        for (int j = 0; j < TT; ++j) *reinterpret_cast<half8_t*>(p + j * kXTile) = xs[j];
+        for (int j = 0; j < TT; ++j) *reinterpret_cast<half8_t*>(p + j * kXTile) = x[j];
     };
 
     float4_t acc[NMAT][TT];
@@ -256,7 +284,14 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[mat][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    // B operands of column group q from a ring slot, and their odd halves
+    // B operands of column group q from a ring slot (lane group g holds the
+    // columns 32g + 8q + 0..7 of the step)
+    auto b_tiles = [&](int slot, int q, half8_t (&bx)[TT]) {
+        const char* p = ring + slot * (TT * kXTile) + i * kXRow + 64 * g + 16 * q;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) bx[tt] = *reinterpret_cast<const half8_t*>(p + tt * kXTile);
+    };
+    // ... and with their odd halves moved down one half (upper halves zero)
     auto b_ops = [&](int slot, int q, half8_t (&bx)[TT], half8_t (&bo)[TT]) {
         const char* p = ring + slot * (TT * kXTile) + i * kXRow + 64 * g + 16 * q;
 #pragma unroll
@@ -271,22 +306,26 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
 
     if constexpr (B == 16) {
         half8_t wr[NB][NMAT][4];
+        // fp16 rows: MFMA q takes the step's columns 32q + 8g + 0..7, so each
+        // load instruction reads 64 contiguous bytes of every row
         auto w_load = [&](half8_t (&w)[NMAT][4], int s) {   // idle waves and steps past s1 read zeros
             const uint32_t n = (live && s < s1) ? mv.wbytes : 0u;
-            const int word = 4 * s + g;
-            const uint32_t base = ((uint32_t)(rowc + i) * (uint32_t)sh.K + 32u * word) * 2u;
+            const uint32_t base = ((uint32_t)(rowc + i) * (uint32_t)sh.K + 128u * s + 8u * g) * 2u;
 #pragma unroll
             for (int mat = 0; mat < NMAT; ++mat) {
                 const __amdgpu_buffer_rsrc_t r = make_rsrc(mv.w16[mat], n);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) w[mat][q] = buf_load_h8(r, word < sh.Wd ? base + 16u * q : kOutOfRange);
+                for (int q = 0; q < 4; ++q)
+                    w[mat][q] = buf_load_h8(r, 4 * s + q < sh.Wd ? base + 64u * q : kOutOfRange);
             }
         };
         auto compute = [&](const half8_t (&w)[NMAT][4], int slot) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                half8_t bx[TT], bo[TT];
-                b_ops(slot, q, bx, bo);
+                half8_t bx[TT];
+                const char* p = ring + slot * (TT * kXTile) + i * kXRow + 64 * q + 16 * g;
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) bx[tt] = *reinterpret_cast<const half8_t*>(p + tt * kXTile);
 #pragma unroll
                 for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
@@ -294,19 +333,20 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
                         acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[mat][q], bx[tt], acc[mat][tt], 0, 0, 0);
             }
         };
-        x_load(s0);
+        x_load(xs[0], s0);
+        x_load(xs[1], s0 + 1);
 #pragma unroll
         for (int u = 0; u < D; ++u) w_load(wr[u], s0 + u);
-        x_store(0);
+        x_store(xs[0], 0);
         __syncthreads();
         for (int s = s0; s < s1; s += NB) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
                 const int st = s + u;   // past s1 (the last group's tail): loads read zeros, no MFMAs
-                x_load(st + 1);
+                x_load(xs[u % 2], st + 2);
                 w_load(wr[(u + D) % NB], st + D);
                 if (live && st < s1) compute(wr[u], (st - s0) & 1);
-                x_store((st + 1 - s0) & 1);
+                x_store(xs[(u + 1) % 2], (st + 1 - s0) & 1);
                 __syncthreads();
             }
         }
@@ -321,7 +361,7 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
             for (int mat = 0; mat < NMAT; ++mat) {
                 const __amdgpu_buffer_rsrc_t r = make_rsrc(mv.planes[mat], n);
 #pragma unroll
-                for (int p = 0; p < B; ++p) w[mat][p] = buf_load_u32(r, p * slab + at);
+                for (int p = 0; p < B; ++p) w[mat][p] = buf_load_u32(r, at, p * slab);
             }
         };
         // lookup address: byte 0 = lane slot offset, byte 1 = code, byte 2 = LUT block
@@ -332,45 +372,66 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
             for (int mat = 0; mat < NMAT; ++mat) {
 #pragma unroll
                 for (int rr = 0; rr < 8; ++rr) qv[mat][rr] = rr < B ? w[mat][B - 1 - rr] : 0u;  // bit rr <- plane B-1-rr
-                transpose_bytes(qv[mat]);
+                transpose_bytes<B>(qv[mat]);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                half8_t bx[TT], bo[TT];
-                b_ops(slot, q, bx, bo);
                 const uint32_t sel = 0x0C020400u | ((uint32_t)q << 8);
+                if constexpr (TT == 1) {
+                    half8_t bx[TT], bo[TT];
+                    b_ops(slot, q, bx, bo);
 #pragma unroll
-                for (int mat = 0; mat < NMAT; ++mat) {
-                    uint32x4_t ev, od;
+                    for (int mat = 0; mat < NMAT; ++mat) {
+                        uint32x4_t ev, od;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        ev[c] = *reinterpret_cast<const uint16_t*>(lds + 2 * mat +
-                                                                   __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
-                        od[c] = *reinterpret_cast<const uint16_t*>(lds + 2 * mat +
-                                                                   __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
+                        for (int c = 0; c < 4; ++c) {
+                            ev[c] = *reinterpret_cast<const uint16_t*>(
+                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
+                            od[c] = *reinterpret_cast<const uint16_t*>(
+                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
+                        }
+                        const half8_t ae = __builtin_bit_cast(half8_t, ev), ao = __builtin_bit_cast(half8_t, od);
+                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bx[0], acc[mat][0], 0, 0, 0);
+                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo[0], acc[mat][0], 0, 0, 0);
                     }
-                    const half8_t ae = __builtin_bit_cast(half8_t, ev), ao = __builtin_bit_cast(half8_t, od);
+                } else {
+                    // several tiles: pack the pairs once (one permute per two
+                    // lookups) and run one MFMA per tile instead of two
+                    half8_t bx[TT];
+                    b_tiles(slot, q, bx);
 #pragma unroll
-                    for (int tt = 0; tt < TT; ++tt) {
-                        acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bx[tt], acc[mat][tt], 0, 0, 0);
-                        acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo[tt], acc[mat][tt], 0, 0, 0);
+                    for (int mat = 0; mat < NMAT; ++mat) {
+                        uint32x4_t w;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint32_t lo = *reinterpret_cast<const uint16_t*>(
+                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
+                            const uint32_t hi = *reinterpret_cast<const uint16_t*>(
+                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
+                            w[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                        }
+                        const half8_t aw = __builtin_bit_cast(half8_t, w);
+#pragma unroll
+                        for (int tt = 0; tt < TT; ++tt)
+                            acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bx[tt], acc[mat][tt], 0, 0, 0);
                     }
                 }
             }
         };
-        x_load(s0);
+        x_load(xs[0], s0);
+        x_load(xs[1], s0 + 1);
 #pragma unroll
         for (int u = 0; u < D; ++u) p_load(pw[u], s0 + u);
-        x_store(0);
+        x_store(xs[0], 0);
         __syncthreads();   // also publishes the LUT tables
         for (int s = s0; s < s1; s += NB) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
                 const int st = s + u;   // past s1 (the last group's tail): loads read zeros, no MFMAs
-                x_load(st + 1);
+                x_load(xs[u % 2], st + 2);
                 p_load(pw[(u + D) % NB], st + D);
                 if (live && st < s1) compute(pw[u], (st - s0) & 1);
-                x_store((st + 1 - s0) & 1);
+                x_store(xs[(u + 1) % 2], (st + 1 - s0) & 1);
                 __syncthreads();
             }
         }

@@ -127,12 +127,17 @@ class MoELayer:
         self.Y = torch.empty((S, H), dtype=torch.float32, **dev)
         self.out = torch.empty((T, H), dtype=torch.float16, **dev)
         nws = _lib.workspace_bytes(T, k, E, H, I)
-        if shared_I:
-            nws = max(nws, _lib.workspace_bytes(T, 1, 1, H, shared_I))
         self.ws = torch.empty(nws, dtype=torch.uint8, **dev) if nws else None
         self.shared = shared
         self.shared_I = shared_I
         if shared is not None:
+            # the shared expert runs on a side stream (default priority) with
+            # its own workspace, overlapping routing and the routed experts
+            self.side = torch.cuda.Stream(device=device)
+            self.ev_fork = torch.cuda.Event()
+            self.ev_join = torch.cuda.Event()
+            nws_sh = _lib.workspace_bytes(T, 1, 1, H, shared_I)
+            self.ws_sh = torch.empty(nws_sh, dtype=torch.uint8, **dev) if nws_sh else None
             self.sh_bits = torch.tensor([16], dtype=torch.int8, **dev)
             self.sh_offsets = torch.tensor([0, T], dtype=torch.int32, **dev)
             self.sh_slots = torch.arange(T, dtype=torch.int32, **dev)
@@ -146,22 +151,31 @@ class MoELayer:
         """x: device fp16 [T, H].  Returns the fp16 output [T, H] (a buffer reused by later calls)."""
         ex = self.experts if experts is None else experts
         sh = self.shared if shared is None else shared
+        import torch
         T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
+        ysh = None
+        if sh is not None:
+            main = torch.cuda.current_stream()
+            self.ev_fork.record(main)
+            self.side.wait_event(self.ev_fork)
+            x.record_stream(self.side)
+            with torch.cuda.stream(self.side):
+                _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, sh.desc, self.sh_bits, 1, self.sh_offsets,
+                                       self.sh_slots, 1, x, self.A_sh, T, H, self.shared_I,
+                                       self.mfma_min_tokens, self.ws_sh)
+                _lib.bitplane_lut_gemm(_lib.DOWN, sh.desc, self.sh_bits, 1, self.sh_offsets, self.sh_slots,
+                                       1, self.A_sh, self.Y_sh, T, H, self.shared_I, self.mfma_min_tokens,
+                                       self.ws_sh)
+            self.ev_join.record(self.side)
+            ysh = self.Y_sh
         _lib.route(x, self.w_router, self.bias, self.logit_scale, k, self.topk_ids, self.topk_w)
         _lib.permute(self.topk_ids, E, self.counts, self.offsets, self.sorted_slots, self.pos_of_slot)
         _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, ex.desc, self.bits, E, self.offsets, self.sorted_slots,
                                k, x, self.A, T, H, I, self.mfma_min_tokens, self.ws)
         _lib.bitplane_lut_gemm(_lib.DOWN, ex.desc, self.bits, E, self.offsets, self.sorted_slots,
                                k, self.A, self.Y, T, H, I, self.mfma_min_tokens, self.ws)
-        ysh = None
         if sh is not None:
-            _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, sh.desc, self.sh_bits, 1, self.sh_offsets,
-                                   self.sh_slots, 1, x, self.A_sh, T, H, self.shared_I,
-                                   self.mfma_min_tokens, self.ws)
-            _lib.bitplane_lut_gemm(_lib.DOWN, sh.desc, self.sh_bits, 1, self.sh_offsets, self.sh_slots,
-                                   1, self.A_sh, self.Y_sh, T, H, self.shared_I, self.mfma_min_tokens,
-                                   self.ws)
-            ysh = self.Y_sh
+            torch.cuda.current_stream().wait_event(self.ev_join)
         _lib.combine(self.Y, self.pos_of_slot, self.topk_w, T, k, H, ysh, self.out)
         return self.out
 

@@ -128,48 +128,69 @@ def main():
 
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    side = getattr(layer, "side", None)           # the shared expert's stream
+    sp2 = side.cuda_stream if side is not None else None
+    ev_fork, ev_join = torch.cuda.Event(), torch.cuda.Event()
     lib = _lib._lib()
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     ws, wsb = (p(layer.ws), layer.ws.numel()) if layer.ws is not None else (None, 0)
+    ws_sh = getattr(layer, "ws_sh", None)
+    ws2, wsb2 = (p(ws_sh), ws_sh.numel()) if ws_sh is not None else (None, 0)
 
-    # Every launch of a step as (name, callable) with its raw arguments bound once.
+    # Every launch of a step as (name, callable, stream) with its raw arguments
+    # bound once; "fork"/"join" entries order the shared expert's side stream.
     def launches(r):
         tab, sh = tables[r], shared[r]
-        seq = [
+        seq = []
+        if sh is not None:
+            Is = cfg.shared_I
+            seq.append(("fork", None, None))
+            seq.append(("shared_gate_up", lambda: lib.apmoe_bitplane_lut_gemm(
+                _lib.GATE_UP_SWIGLU, p(sh.desc), p(layer.sh_bits), 1, p(layer.sh_offsets), p(layer.sh_slots), 1,
+                p(x), p(layer.A_sh), T, H, Is, mfma_min, ws2, wsb2, sp2), side))
+            seq.append(("shared_down", lambda: lib.apmoe_bitplane_lut_gemm(
+                _lib.DOWN, p(sh.desc), p(layer.sh_bits), 1, p(layer.sh_offsets), p(layer.sh_slots), 1,
+                p(layer.A_sh), p(layer.Y_sh), T, H, Is, mfma_min, ws2, wsb2, sp2), side))
+            seq.append(("side_done", None, None))
+        seq += [
             ("route", lambda: lib.apmoe_route(p(x), T, H, p(layer.w_router), p(layer.bias), layer.logit_scale,
-                                              E, k, p(layer.topk_ids), p(layer.topk_w), sp)),
+                                              E, k, p(layer.topk_ids), p(layer.topk_w), sp), stream),
             ("permute", lambda: lib.apmoe_permute(p(layer.topk_ids), T, k, E, p(layer.counts), p(layer.offsets),
-                                                  p(layer.sorted_slots), p(layer.pos_of_slot), None, 0, sp)),
+                                                  p(layer.sorted_slots), p(layer.pos_of_slot), None, 0, sp), stream),
         ]
         for stage, name, src, dst in ((_lib.GATE_UP_SWIGLU, "gate_up", x, layer.A),
                                       (_lib.DOWN, "down", layer.A, layer.Y)):
             for flag, path in ((_lib.ONLY_GEMV, "gemv"), (_lib.ONLY_TILE, "tile")):
                 seq.append((f"{name}_{path}", (lambda st=stage | flag, s_=src, d_=dst: lib.apmoe_bitplane_lut_gemm(
                     st, p(tab.desc), p(layer.bits), E, p(layer.offsets), p(layer.sorted_slots), k, p(s_), p(d_),
-                    T, H, I, mfma_min, ws, wsb, sp))))
-        if sh is not None:
-            Is = cfg.shared_I
-            seq.append(("shared_gate_up", lambda: lib.apmoe_bitplane_lut_gemm(
-                _lib.GATE_UP_SWIGLU, p(sh.desc), p(layer.sh_bits), 1, p(layer.sh_offsets), p(layer.sh_slots), 1,
-                p(x), p(layer.A_sh), T, H, Is, mfma_min, ws, wsb, sp)))
-            seq.append(("shared_down", lambda: lib.apmoe_bitplane_lut_gemm(
-                _lib.DOWN, p(sh.desc), p(layer.sh_bits), 1, p(layer.sh_offsets), p(layer.sh_slots), 1,
-                p(layer.A_sh), p(layer.Y_sh), T, H, Is, mfma_min, ws, wsb, sp)))
+                    T, H, I, mfma_min, ws, wsb, sp)), stream))
         ysh = p(layer.Y_sh) if sh is not None else None
+        if sh is not None:
+            seq.append(("join", None, None))
         seq.append(("combine", lambda: lib.apmoe_combine(p(layer.Y), p(layer.pos_of_slot), p(layer.topk_w), T, k,
-                                                          H, ysh, p(layer.out), sp)))
+                                                          H, ysh, p(layer.out), sp), stream))
         return seq
 
     steps = [launches(r) for r in range(R)]
-    names = [n for n, _ in steps[0]]
+    names = [n for n, fn, _ in steps[0] if fn is not None]
 
     def run(seq, timed_name=None, ev=None):
-        for n, fn in seq:
-            if n == timed_name:
-                ev[0].record(stream)
+        for n, fn, st in seq:
+            if n == "fork":
+                ev_fork.record(stream)
+                side.wait_event(ev_fork)
+                continue
+            if n == "side_done":
+                ev_join.record(side)
+                continue
+            if n == "join":
+                stream.wait_event(ev_join)
+                continue
+            if n == timed_name:   # events on the stream the launch runs on
+                ev[0].record(st)
                 rc = fn()
-                ev[1].record(stream)
+                ev[1].record(st)
             else:
                 rc = fn()
             if rc != 0:
