@@ -43,7 +43,8 @@ def _lib():
                                "`python -m any_precision_quantized_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
         sig = {
-            "apmoe_route": [_vp, _c_int, _c_int, _vp, _vp, ctypes.c_float, _c_int, _c_int, _vp, _vp, _vp],
+            "apmoe_route": [_vp, _c_int, _c_int, _vp, _vp, ctypes.c_float, _c_int, _c_int, _vp, _vp, _vp,
+                            _c_size, _vp],
             "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp],
             "apmoe_bitplane_lut_gemm": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                         _c_int, _c_int, _c_int, _vp, _c_size, _vp],
@@ -115,15 +116,16 @@ def _stream(stream=None):
 # Entry points (same names as the C ABI, without the prefix)
 # ---------------------------------------------------------------------------
 
-def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, stream=None):
+def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, ws=None, stream=None):
     torch = _torch()
     T, H = x.shape
     E = w_router.shape[0]
+    wsp, wsb = (None, 0) if ws is None else (_ptr(ws, torch.uint8, ws.numel(), "ws"), ws.numel())
     rc = _lib().apmoe_route(_ptr(x, torch.float16, T * H, "x"), T, H,
                             _ptr(w_router, torch.float32, E * H, "w_router"),
                             _ptr(bias, torch.float32, E, "bias"), float(logit_scale), E, k,
                             _ptr(topk_ids, torch.int32, T * k, "topk_ids"),
-                            _ptr(topk_w, torch.float32, T * k, "topk_w"), _stream(stream))
+                            _ptr(topk_w, torch.float32, T * k, "topk_w"), wsp, wsb, _stream(stream))
     _check(rc, "apmoe_route")
 
 

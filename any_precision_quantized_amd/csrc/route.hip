@@ -1,83 +1,96 @@
 // Router: top-k over the router logits, then a softmax over the k chosen.
 //
-// One workgroup (4 waves) per token.  Lanes split the hidden dimension and the
-// waves split the experts: wave w accumulates, for experts e = w, w+4, ...,
-// the products of its lanes' slice in fp64 (fp16 x fp32 products are exact in
-// fp64), up to 16 experts at once so their loads overlap.  Per-lane partials meet in
-// LDS and one thread per expert adds the 64 lane partials in lane order, so
-// the logit is a fixed-order fp64 sum.  Then one wave runs k rounds of a
-// wave-wide argmax (ties to the lower expert) and the softmax over the k.
+// Two kernels.  The logits kernel tiles (4 tokens x 8 experts) per workgroup:
+// wave w owns experts 2w, 2w+1 of the tile and its lanes split the hidden
+// dimension (four columns each per 256), so one 16-byte router-weight load
+// feeds four tokens and the tile's weights and activations cross the CU once.
+// Products and sums are fp64 (an fp16 x fp32 product is exact in fp64); each
+// lane's partial sums meet in a fixed xor butterfly, so a logit never depends
+// on scheduling.  The logits go to the workspace; the select kernel then runs
+// one wave per token: k rounds of a wave-wide argmax (ties to the lower
+// expert), then the softmax over the k chosen logits in fp64.
 #include "common.hpp"
 
 namespace apmoe {
+namespace {
 
-constexpr int kRouteWaves = 4;
-constexpr int kRouteChunk = 64;      // experts reduced per LDS round
+constexpr int kTB = 4;                  // tokens per logits tile
+constexpr int kEPW = 2;                 // experts per wave
+constexpr int kRWaves = 4;
+constexpr int kEB = kEPW * kRWaves;     // experts per logits tile
 
-__global__ __launch_bounds__(kRouteWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 2))) void route_kernel(
-    const half_t* __restrict__ x, int T, int H, const float* __restrict__ w_router,
-    const float* __restrict__ bias, float scale, int E, int k, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_w) {
-    __shared__ double red[kRouteChunk][kWave + 1];
-    __shared__ double logits[APMOE_MAX_EXPERTS];
-    __shared__ double chosen[APMOE_MAX_EXPERTS];
-    const int t = blockIdx.x;
+typedef float float4v_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* __restrict__ x, int T, int H,
+                                                                  const float* __restrict__ w_router,
+                                                                  const float* __restrict__ bias, float scale,
+                                                                  int E, double* __restrict__ L) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int t0 = blockIdx.x * kTB;
+    const int e0 = blockIdx.y * kEB + wave * kEPW;
+    // rows past T or E read a valid row; their sums are never written
+    const half_t* xr[kTB];
+#pragma unroll
+    for (int j = 0; j < kTB; ++j) xr[j] = x + (size_t)min(t0 + j, T - 1) * H;
+    const float* wr[kEPW];
+#pragma unroll
+    for (int j = 0; j < kEPW; ++j) wr[j] = w_router + (size_t)min(e0 + j, E - 1) * H;
+
+    double acc[kTB][kEPW];
+#pragma unroll
+    for (int t = 0; t < kTB; ++t)
+#pragma unroll
+        for (int j = 0; j < kEPW; ++j) acc[t][j] = 0.0;
+#pragma unroll 2
+    for (int h = 4 * lane; h < H; h += 4 * kWave) {   // H % 32 == 0: h + 3 < H
+        float4v_t wv[kEPW];
+#pragma unroll
+        for (int j = 0; j < kEPW; ++j) wv[j] = *reinterpret_cast<const float4v_t*>(wr[j] + h);
+#pragma unroll
+        for (int t = 0; t < kTB; ++t) {
+            const half4_t xv = *reinterpret_cast<const half4_t*>(xr[t] + h);
+#pragma unroll
+            for (int j = 0; j < kEPW; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[t][j] = fma((double)xv[c], (double)wv[j][c], acc[t][j]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kTB; ++t)
+#pragma unroll
+        for (int j = 0; j < kEPW; ++j) {
+            const double s = wave_sum(acc[t][j]);
+            const int tt = t0 + t, e = e0 + j;
+            if (lane == 0 && tt < T && e < E)
+                L[(size_t)tt * E + e] = (double)scale * (s + (bias ? (double)bias[e] : 0.0));
+        }
+}
+
+constexpr int kSelWaves = 4;
+
+__global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double* __restrict__ L, int T, int E, int k,
+                                                                    int32_t* __restrict__ topk_ids,
+                                                                    float* __restrict__ topk_w) {
+    __shared__ double chosen[kSelWaves][APMOE_MAX_EXPERTS];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const half_t* xt = x + (size_t)t * H;
-
-    // Experts in chunks of 64 (one LDS round each); wave w owns experts
-    // c0 + w + 4 j, j < 16, and walks H eight columns per lane at a time with
-    // every load of the chunk independent.
-    const int uw = __builtin_amdgcn_readfirstlane(wave);
-    for (int c0 = 0; c0 < E; c0 += kRouteChunk) {
-        const int ce = min(kRouteChunk, E - c0);
-        double acc[kRouteChunk / kRouteWaves];
+    const int t = blockIdx.x * kSelWaves + wave;
+    if (t >= T) return;   // uniform over the wave; no block barrier follows
+    constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
+    double v[kPer];
 #pragma unroll
-        for (int j = 0; j < kRouteChunk / kRouteWaves; ++j) acc[j] = 0.0;
-        for (int h0 = 0; h0 < H; h0 += 8 * kWave) {
-            // columns past H: address clamped, activation zero (no branches,
-            // so every load of the chunk is in flight at once)
-            double xv[8];
-            int hc[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int h = h0 + lane + kWave * u;
-                hc[u] = min(h, H - 1);
-                const double v = (double)xt[hc[u]];
-                xv[u] = h < H ? v : 0.0;
-            }
-#pragma unroll
-            for (int j = 0; j < kRouteChunk / kRouteWaves; ++j) {
-                // experts past the chunk read a valid row; their sums are dropped below
-                const int el = min(uw + kRouteWaves * j, ce - 1);
-                const float* w = w_router + (size_t)(c0 + el) * H;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) acc[j] = fma(xv[u], (double)w[hc[u]], acc[j]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kRouteChunk / kRouteWaves; ++j) {
-            const int el = uw + kRouteWaves * j;
-            if (el < ce) red[el][lane] = acc[j];
-        }
-        __syncthreads();
-        if (threadIdx.x < ce) {
-            double s = 0.0;
-            for (int l = 0; l < kWave; ++l) s += red[threadIdx.x][l];
-            const int e = c0 + threadIdx.x;
-            logits[e] = (double)scale * (s + (bias ? (double)bias[e] : 0.0));
-        }
-        __syncthreads();
+    for (int c = 0; c < kPer; ++c) {
+        const int e = lane + kWave * c;
+        v[c] = e < E ? L[(size_t)t * E + e] : -__builtin_inf();
     }
-    if (wave != 0) return;   // no block barrier follows
-
     for (int j = 0; j < k; ++j) {
         double best = -__builtin_inf();
         int best_e = E;
-        for (int e = lane; e < E; e += kWave) {
-            const double v = logits[e];
-            if (v > best || (v == best && e < best_e)) { best = v; best_e = e; }
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) {   // ascending e within the lane: ties keep the lower
+            const int e = lane + kWave * c;
+            if (e < E && (v[c] > best || (v[c] == best && e < best_e))) { best = v[c]; best_e = e; }
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
@@ -85,36 +98,47 @@ __global__ __launch_bounds__(kRouteWaves * kWave) __attribute__((amdgpu_waves_pe
             const int oe = __shfl_xor(best_e, o, kWave);
             if (ov > best || (ov == best && oe < best_e)) { best = ov; best_e = oe; }
         }
+        // every lane holds the same winner; its owner drops it from the race
+#pragma unroll
+        for (int c = 0; c < kPer; ++c)
+            if (lane + kWave * c == best_e) v[c] = -__builtin_inf();
         if (lane == 0) {
-            chosen[j] = best;
-            logits[best_e] = -__builtin_inf();
+            chosen[wave][j] = best;
             topk_ids[(size_t)t * k + j] = best_e;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (lane == 0) {
-        const double lmax = chosen[0];
+        const double lmax = chosen[wave][0];
         double sum = 0.0;
-        for (int j = 0; j < k; ++j) sum += exp(chosen[j] - lmax);
-        for (int j = 0; j < k; ++j) topk_w[(size_t)t * k + j] = (float)(exp(chosen[j] - lmax) / sum);
+        for (int j = 0; j < k; ++j) sum += exp(chosen[wave][j] - lmax);
+        for (int j = 0; j < k; ++j) topk_w[(size_t)t * k + j] = (float)(exp(chosen[wave][j] - lmax) / sum);
     }
 }
+
+}  // namespace
+
+size_t route_workspace_bytes(int T, int E) { return (size_t)(T > 0 ? T : 0) * (size_t)(E > 0 ? E : 0) * sizeof(double); }
 
 }  // namespace apmoe
 
 using namespace apmoe;
 
 extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const float* bias,
-                           float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w,
-                           void* stream) {
-    if (T < 0 || H <= 0 || E < 1 || E > APMOE_MAX_EXPERTS || k < 1 || k > E) return APMOE_EINVAL;
+                           float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, void* ws,
+                           size_t ws_bytes, void* stream) {
+    if (T < 0 || H <= 0 || H % 32 || E < 1 || E > APMOE_MAX_EXPERTS || k < 1 || k > E) return APMOE_EINVAL;
     if (!(logit_scale > 0.0f)) return APMOE_EINVAL;
     if (T == 0) return APMOE_OK;
     if (!x || !w_router || !topk_ids || !topk_w) return APMOE_EINVAL;
-    hipLaunchKernelGGL(route_kernel, dim3(T), dim3(kRouteWaves * kWave), 0, as_stream(stream),
-                       reinterpret_cast<const half_t*>(x), T, H, w_router, bias, logit_scale, E, k,
-                       topk_ids, topk_w);
+    if (!ws || ws_bytes < route_workspace_bytes(T, E)) return APMOE_ENOSPACE;
+    hipStream_t s = as_stream(stream);
+    double* L = reinterpret_cast<double*>(ws);
+    dim3 grid((T + kTB - 1) / kTB, (E + kEB - 1) / kEB);
+    hipLaunchKernelGGL(logits_kernel, grid, dim3(kRWaves * kWave), 0, s, reinterpret_cast<const half_t*>(x), T, H,
+                       w_router, bias, logit_scale, E, L);
+    int rc = launch_status();
+    if (rc != APMOE_OK) return rc;
+    hipLaunchKernelGGL(select_kernel, dim3((T + kSelWaves - 1) / kSelWaves), dim3(kSelWaves * kWave), 0, s, L, T, E,
+                       k, topk_ids, topk_w);
     return launch_status();
 }

@@ -168,7 +168,7 @@ class MoELayer:
                                        self.ws_sh)
             self.ev_join.record(self.side)
             ysh = self.Y_sh
-        _lib.route(x, self.w_router, self.bias, self.logit_scale, k, self.topk_ids, self.topk_w)
+        _lib.route(x, self.w_router, self.bias, self.logit_scale, k, self.topk_ids, self.topk_w, self.ws)
         _lib.permute(self.topk_ids, E, self.counts, self.offsets, self.sorted_slots, self.pos_of_slot)
         _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, ex.desc, self.bits, E, self.offsets, self.sorted_slots,
                                k, x, self.A, T, H, I, self.mfma_min_tokens, self.ws)

@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--workload", default="qwen_decode")
     ap.add_argument("--mfma-min-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial-shared", action="store_true",
+                    help="run the shared expert on the main stream instead of the side stream")
     ap.add_argument("--replica-bytes", type=float, default=1.0e9,
                     help="weight bytes the rotating replicas must span (MALL defeat)")
     args = ap.parse_args()
@@ -129,6 +131,8 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     side = getattr(layer, "side", None)           # the shared expert's stream
+    if args.serial_shared and side is not None:
+        side = stream
     sp2 = side.cuda_stream if side is not None else None
     ev_fork, ev_join = torch.cuda.Event(), torch.cuda.Event()
     lib = _lib._lib()
@@ -155,7 +159,7 @@ def main():
             seq.append(("side_done", None, None))
         seq += [
             ("route", lambda: lib.apmoe_route(p(x), T, H, p(layer.w_router), p(layer.bias), layer.logit_scale,
-                                              E, k, p(layer.topk_ids), p(layer.topk_w), sp), stream),
+                                              E, k, p(layer.topk_ids), p(layer.topk_w), ws, wsb, sp), stream),
             ("permute", lambda: lib.apmoe_permute(p(layer.topk_ids), T, k, E, p(layer.counts), p(layer.offsets),
                                                   p(layer.sorted_slots), p(layer.pos_of_slot), None, 0, sp), stream),
         ]

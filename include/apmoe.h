@@ -90,10 +90,13 @@ typedef struct apmoe_expert {
  *  x        fp16 [T][H]          w_router fp32 [E][H]
  *  bias     fp32 [E] or NULL     logit_scale > 0
  *  topk_ids int32 [T][k] (out)   topk_w   fp32 [T][k] (out)
- * Needs 1 <= k <= E <= APMOE_MAX_EXPERTS, H > 0.
+ *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I)
+ *           bytes (the fp64 logits, T * E * 8 bytes); APMOE_ENOSPACE if short.
+ * Needs 1 <= k <= E <= APMOE_MAX_EXPERTS, H > 0 and H % 32 == 0.
  */
 int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const float* bias,
-                float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, void* stream);
+                float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, void* ws,
+                size_t ws_bytes, void* stream);
 
 /*
  * Group slots by expert (stable: within an expert, slots in ascending order).
@@ -168,7 +171,8 @@ int apmoe_plan_bitwidths(int E, int L, const int8_t* levels, const double* harm,
  */
 int apmoe_commit_bits(const int8_t* bits_host, int E, int8_t* bits_dev, void* stream);
 
-/* Workspace bytes apmoe_bitplane_lut_gemm needs for these shapes. */
+/* Workspace bytes apmoe_route and apmoe_bitplane_lut_gemm need for these
+ * shapes (one buffer serves both; calls that share it must not overlap). */
 size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I);
 
 /* uint32 words of all six packed planes of a rows x cols matrix:

@@ -38,11 +38,16 @@ def test_validation_before_launch():
     lib = _lib._lib()
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
     # route: k > E, bad scale, null pointers
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 9, fake, fake, None) == _lib.EINVAL
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 0.0, 8, 2, fake, fake, None) == _lib.EINVAL
-    assert lib.apmoe_route(None, 4, 64, fake, None, 1.0, 8, 2, fake, fake, None) == _lib.EINVAL
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 300, 2, fake, fake, None) == _lib.EINVAL
-    assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None) == _lib.OK   # T = 0
+    big = 1 << 20
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 9, fake, fake, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 0.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(None, 4, 64, fake, None, 1.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 300, 2, fake, fake, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 48, fake, None, 1.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL   # H % 32
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 2, fake, fake, fake, 4 * 8 * 8 - 1, None) == _lib.ENOSPACE
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 2, fake, fake, None, big, None) == _lib.ENOSPACE
+    assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None, 0, None) == _lib.OK   # T = 0
+    assert _lib.workspace_bytes(4, 2, 8, 64, 64) >= 4 * 8 * 8
     # permute
     assert lib.apmoe_permute(fake, 4, 0, 8, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
     assert lib.apmoe_permute(None, 4, 2, 8, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
