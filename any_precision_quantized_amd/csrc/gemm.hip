@@ -4,152 +4,314 @@
 // Dispatch happens on the device: every workgroup reads its expert's slot
 // count and bitwidth and leaves at once when the group is empty or belongs to
 // the other path, so no count ever travels to the host.
+#include <algorithm>
+
 #include "common.hpp"
+#include "decode.hpp"
 
 namespace apmoe {
 
 // ---------------------------------------------------------------------------
-// Tile path (groups of at least mfma_min_tokens): the weight tile is decoded
-// into LDS as exact fp16 and multiplied with v_mfma_f32_16x16x16_f16.
-//   D[token][row] = sum_k X[token][k] * W[row][k]
-// Workgroup tile 64 tokens x 64 rows, K step 32, 4 waves each 32 x 32.
+// Tile path (groups of at least mfma_min_tokens): every K step the weight
+// tile is decoded from the bit-planes into LDS as exact fp16 and multiplied
+// with v_mfma_f32_32x32x16_f16 against an LDS tile of the group's tokens.
+//   D[row][token] = sum_k W[row][k] * X[token][k]
+// Workgroup tile: 256 weight rows x 256 tokens, K step 32 (one plane word
+// per row).  For gate/up the 256 rows are 128 gate rows and the same 128 up
+// rows, so the SwiGLU pairs meet in one lane.  Four waves each own 128 rows
+// x 128 tokens (4 x 4 MFMA tiles, 256 fp32 accumulators per lane).  Thread t
+// decodes row t of the weight tile (its b plane words, the same byte
+// transpose and LUT-in-LDS lookups as the GEMV path) and stages token t of
+// the activation tile.  Weight and activation loads run two steps ahead in
+// a register ring; the two LDS stages alternate, one barrier per step.
+// Items are (expert, row tile, token tile) with the token tile fastest, so
+// the workgroups the dispatcher sends to one XCD share that XCD's L2 copy of
+// a token tile while all XCDs walk the same weight rows.
 // ---------------------------------------------------------------------------
 
-constexpr int kBM = 64, kBN = 64, kBK = 32, kLdsPad = 8;
+namespace {
 
-template <int NMAT>
-__global__ __launch_bounds__(256) void tile_simple_kernel(GemmArgs a) {
+constexpr int kThreadsTile = 256;
+constexpr int kTRows = 256;              // weight rows per tile (gate/up: 128 + 128)
+constexpr int kTToks = 256;              // tokens per tile
+constexpr int kRowB = 80;                // LDS bytes per tile row: 32 halves + 16 pad
+constexpr int kTileB = 256 * kRowB;
+// LDS map: LUT block 0 | W0 | X0 at 0, 16K, 36K; LUT block 1 | W1 | X1 at
+// 64K, 80K, 100K (the lookup permute puts the LUT block into address byte 2).
+constexpr int kStageOff[2] = {16384, 81920};
+constexpr int kTileLds = 81920 + 2 * kTileB;
+static_assert(16384 + 2 * kTileB <= 65536, "stage 0 overlaps LUT block 1");
+
+struct TileItem {
+    int e, off, m, b, rt, tt;
+};
+
+// Item of workgroup idx over the groups on this path, each owning
+// ceil(m / 256) x RT items in (row tile, token tile) order.
+__device__ __forceinline__ bool find_tile_item(const GemmArgs& a, int RT, int idx, TileItem& it) {
+    const int lane = threadIdx.x % kWave;
+    int base = 0;
+    for (int c0 = 0; c0 < a.E; c0 += kWave) {
+        const int e = c0 + lane;
+        int m = 0, b = 0;
+        if (e < a.E) {
+            m = a.offsets[e + 1] - a.offsets[e];
+            b = a.bits[e];
+        }
+        const int nt = (m + kTToks - 1) / kTToks;
+        const int n = (m > 0 && m >= a.mfma_min_tokens && valid_bits(b)) ? nt * RT : 0;
+        int inc = n;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int t = __shfl_up(inc, o, kWave);
+            if (lane >= o) inc += t;
+        }
+        const int first = base + inc - n;
+        const unsigned long long hit = __ballot(n > 0 && idx >= first && idx < first + n);
+        if (hit) {
+            const int src = __ffsll((long long)hit) - 1;
+            it.e = __builtin_amdgcn_readfirstlane(c0 + src);
+            it.m = __builtin_amdgcn_readfirstlane(__shfl(m, src, kWave));
+            it.b = __builtin_amdgcn_readfirstlane(__shfl(b, src, kWave));
+            const int q = __builtin_amdgcn_readfirstlane(idx - __shfl(first, src, kWave));
+            const int ntile = (it.m + kTToks - 1) / kTToks;
+            it.rt = q / ntile;
+            it.tt = q % ntile;
+            it.off = a.offsets[it.e];
+            return true;
+        }
+        base += __shfl(inc, kWave - 1, kWave);
+    }
+    return false;
+}
+
+template <int NMAT, int B>
+__device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const TileItem& it) {
+    constexpr int kMatRows = NMAT == 2 ? 128 : 256;   // rows of one matrix in the tile
     const int rows = NMAT == 2 ? a.I : a.H;
     const int K = NMAT == 2 ? a.H : a.I;
-    const int W = K / 32;
-    const int n0 = blockIdx.x * kBN;
-
-    // Nothing to do unless some group reaches the threshold: one wave-wide
-    // vote per 64 experts, before any LDS traffic (uniform over the workgroup).
-    {
-        const int lane = threadIdx.x % kWave;
-        bool any = false;
-        for (int c0 = 0; c0 < a.E && !any; c0 += kWave) {
-            const int e = c0 + lane;
-            const int c = e < a.E ? a.offsets[e + 1] - a.offsets[e] : 0;
-            any = __ballot(c >= a.mfma_min_tokens) != 0;
-        }
-        if (!any) return;
-    }
-    // Map blockIdx.y to (expert, m-tile) over the groups that take this path
-    // (slot counts staged in LDS once, then a scan from LDS).
-    __shared__ int cnt[APMOE_MAX_EXPERTS + 1];
-    for (int ee = threadIdx.x; ee <= a.E; ee += blockDim.x) cnt[ee] = a.offsets[ee];
-    __syncthreads();
-    for (int slot = blockIdx.y; slot < a.T * a.k / kBM + a.E; slot += gridDim.y) {
-    int q = slot, e = -1, m0 = 0, off = 0, m = 0;
-    for (int ee = 0; ee < a.E; ++ee) {
-        const int o = cnt[ee], c = cnt[ee + 1] - o;
-        if (c < a.mfma_min_tokens || c == 0) continue;
-        const int tiles = (c + kBM - 1) / kBM;
-        if (q < tiles) { e = ee; m0 = q * kBM; off = o; m = c; break; }
-        q -= tiles;
-    }
-    if (e < 0) break;   // slots past the last tile: uniform over the workgroup
-    const int b = a.bits[e];
-    if (!valid_bits(b)) continue;
-    MatView mv[NMAT];
-    if (NMAT == 2) {
-        mv[0] = mat_view(a.experts[e].gate, b);
-        mv[NMAT - 1] = mat_view(a.experts[e].up, b);
-    } else {
-        mv[0] = mat_view(a.experts[e].down, b);
-    }
-    const half_t* in = reinterpret_cast<const half_t*>(a.in);
-
-    __shared__ half_t xs[kBM][kBK + kLdsPad];
-    __shared__ half_t ws[NMAT][kBN][kBK + kLdsPad];
-
+    const int ns = K / 32;                    // K steps
+    const int nsteps128 = (K / 32 + 3) / 4;   // steps of the packed plane layout
     const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave / 2, wn = wave % 2;  // 32 x 32 sub-tile of the wave
-    float4_t acc[NMAT][2][2];
-    for (int qq = 0; qq < NMAT; ++qq)
-        for (int i = 0; i < 2; ++i)
-            for (int j = 0; j < 2; ++j) acc[qq][i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int r0 = it.rt * kMatRows, t0 = it.tt * kTToks;
 
-    // Loader roles: thread -> (row or token = tid / 4, eight columns at 8 * (tid % 4)).
-    const int lr = tid / 4, lc = 8 * (tid % 4);
-    const int tok = m0 + lr;
-    const half_t* xsrc = nullptr;
-    if (tok < m) {
-        const int j = off + tok;
-        xsrc = NMAT == 2 ? in + (size_t)(a.sorted_slots[j] / a.k) * K : in + (size_t)j * K;
-    }
-    const int wrow = n0 + lr;
+    // decode role: tile row tid = matrix hsel, row r0 + (tid % kMatRows)
+    const int hsel = NMAT == 2 ? wave >> 1 : 0;   // gate/up: matrix (waves 2, 3: up); down: 0
+    const int rowc = min(r0 + tid % kMatRows, rows - 1);
+    const apmoe_mat& mt = NMAT == 2 ? (hsel ? a.experts[it.e].up : a.experts[it.e].gate) : a.experts[it.e].down;
+    const MatView mv = mat_view(mt, it.b);
+    const uint32_t pbytes = 6u * (uint32_t)rows * 16u * (uint32_t)nsteps128;
+    const uint32_t slab = (uint32_t)rows * 16u * (uint32_t)nsteps128;
+    const uint32_t wbytes = (uint32_t)rows * (uint32_t)K * 2u;
 
-    for (int kw = 0; kw < W; ++kw) {
-        // activations
-        half8_t xv = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (xsrc) xv = *reinterpret_cast<const half8_t*>(xsrc + 32 * kw + lc);
-        // weights
-        half8_t wv[NMAT];
-        for (int qq = 0; qq < NMAT; ++qq) {
-            half8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (wrow < rows) {
-                if (b == 16) {
-                    v = load_h8g(mv[qq].w16 + (size_t)wrow * K + 32 * kw + lc);
-                } else {
-                    uint32_t pw[6];
-                    for (int p = 0; p < b; ++p) pw[p] = mv[qq].planes[packed_index(rows, packed_steps(K), p, wrow, kw)];
-                    gh16_t* lut = mv[qq].lut + (size_t)wrow * (1 << b);
-                    for (int i = 0; i < 8; ++i) v[i] = lut[code_of(pw, b, lc + i)];
-                }
-            }
-            wv[qq] = v;
+    // activation role: token t0 + tid of the group
+    const int tok = t0 + tid;
+    const bool tok_ok = tok < it.m;
+    const int tokc = it.off + min(tok, it.m - 1);
+    const int xrow = NMAT == 2 ? a.sorted_slots[tokc] / a.k : tokc;
+    const uint32_t xbytes = (uint32_t)((NMAT == 2 ? (size_t)a.T : (size_t)a.T * a.k) * K * 2);
+    const uint32_t xbase = (uint32_t)xrow * (uint32_t)K * 2u;
+
+    // LUTs of the tile's rows: entry (code v, row r < 128) at block r / 64,
+    // v * 256 + 4 * (r % 64); low half gate (down: row r), high half up
+    // (down: row r + 128)
+    if constexpr (B != 16) {
+        constexpr int nent = 1 << B;
+        const gu16_t* l0;
+        const gu16_t* l1;
+        if (NMAT == 2) {
+            l0 = (const gu16_t*)mat_view(a.experts[it.e].gate, it.b).lut;
+            l1 = (const gu16_t*)mat_view(a.experts[it.e].up, it.b).lut;
+        } else {
+            l0 = l1 = (const gu16_t*)mv.lut;
         }
-        __syncthreads();
-        *reinterpret_cast<half8_t*>(&xs[lr][lc]) = xv;
-        for (int qq = 0; qq < NMAT; ++qq) *reinterpret_cast<half8_t*>(&ws[qq][lr][lc]) = wv[qq];
-        __syncthreads();
-        for (int kk = 0; kk < kBK; kk += 16) {
-            const int kq = kk + 4 * (lane / 16);
-            half4_t av[2];
-            for (int i = 0; i < 2; ++i)
-                av[i] = *reinterpret_cast<const half4_t*>(&xs[wm * 32 + i * 16 + lane % 16][kq]);
-            for (int qq = 0; qq < NMAT; ++qq) {
-                for (int j = 0; j < 2; ++j) {
-                    const half4_t bv = *reinterpret_cast<const half4_t*>(&ws[qq][wn * 32 + j * 16 + lane % 16][kq]);
-                    for (int i = 0; i < 2; ++i)
-                        acc[qq][i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[i], bv, acc[qq][i][j], 0, 0, 0);
-                }
-            }
+        for (int idx = tid; idx < 128 * nent; idx += kThreadsTile) {
+            const int v = idx / 128, r = idx % 128;
+            const int ra = min(r0 + r, rows - 1);
+            const int rb = NMAT == 2 ? ra : min(r0 + 128 + r, rows - 1);
+            const uint32_t val = (uint32_t)l0[(size_t)ra * nent + v] | ((uint32_t)l1[(size_t)rb * nent + v] << 16);
+            *reinterpret_cast<uint32_t*>(lds + ((r >> 6) << 16) + v * 256 + 4 * (r & 63)) = val;
         }
     }
-    // D lane layout: token = 4 * (lane / 16) + r, row = lane % 16.
-    for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j)
-            for (int r = 0; r < 4; ++r) {
-                const int t = m0 + wm * 32 + i * 16 + 4 * (lane / 16) + r;
-                const int n = n0 + wn * 32 + j * 16 + lane % 16;
-                if (t < m && n < rows) {
-                    const size_t o = (size_t)(off + t) * rows + n;
-                    if (NMAT == 2)
-                        reinterpret_cast<half_t*>(a.out)[o] =
-                            (half_t)(silu_f32(acc[0][i][j][r]) * acc[NMAT - 1][i][j][r]);
-                    else
-                        reinterpret_cast<float*>(a.out)[o] = acc[0][i][j][r];
-                }
+    // lookup address: byte 0 = slot (row % 64) * 4 + 2 * half, byte 1 = code,
+    // byte 2 = LUT block (row / 64 % 2)
+    const uint32_t lane_off = ((uint32_t)(wave & 1) << 16) |
+                              (4u * (uint32_t)lane + 2u * (uint32_t)(NMAT == 2 ? hsel : (wave >> 1)));
+
+    constexpr int WR = B == 16 ? 4 : B;   // registers of one step's weights
+    uint32_t wreg[3][WR > 0 ? WR * (B == 16 ? 4 : 1) : 1];
+    half8_t xreg[3][4];
+    auto load = [&](int r, int s) {   // steps past ns read zeros
+        const bool ok = s < ns;
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.in, ok ? xbytes : 0u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xreg[r][j] = buf_load_h8(xr, tok_ok ? xbase + 64u * s + 16u * j : kOutOfRange);
+        if constexpr (B == 16) {
+            const __amdgpu_buffer_rsrc_t wr = make_rsrc((const void*)mv.w16, ok ? wbytes : 0u);
+            const uint32_t base = ((uint32_t)rowc * (uint32_t)K + 32u * s) * 2u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32x4_t v = __builtin_bit_cast(uint32x4_t, buf_load_h8(wr, base + 16u * j));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) wreg[r][4 * j + c] = v[c];
             }
+        } else {
+            const __amdgpu_buffer_rsrc_t pr = make_rsrc((const void*)mv.planes, ok ? pbytes : 0u);
+            const int sc = min(s, ns - 1);
+            const uint32_t at = ((uint32_t)(rowc >> 4) * (uint32_t)nsteps128 + (uint32_t)(sc >> 2)) * 256u +
+                                64u * (uint32_t)(sc & 3) + 4u * (uint32_t)(rowc & 15);
+#pragma unroll
+            for (int p = 0; p < B; ++p) wreg[r][p] = buf_load_u32(pr, at, p * slab);
+        }
+    };
+    auto store = [&](int r, int st) {   // decode into LDS stage st
+        char* wt = lds + kStageOff[st] + tid * kRowB;
+        char* xt = lds + kStageOff[st] + kTileB + tid * kRowB;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<half8_t*>(xt + 16 * j) = xreg[r][j];
+        if constexpr (B == 16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32x4_t v;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[c] = wreg[r][4 * j + c];
+                *reinterpret_cast<uint32x4_t*>(wt + 16 * j) = v;
+            }
+        } else {
+            uint32_t q[8];
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) q[rr] = rr < B ? wreg[r][B - 1 - rr] : 0u;   // bit rr <- plane B-1-rr
+            transpose_bytes<B>(q);
+            // byte u of q[j] is the code of column 8u + j: eight lookups, four
+            // packed dwords, one 16-byte store per byte lane
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t sel = 0x0C020400u | ((uint32_t)u << 8);
+                uint32x4_t v;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t lo = *reinterpret_cast<const uint16_t*>(lds + __builtin_amdgcn_perm(q[2 * c], lane_off, sel));
+                    const uint32_t hi = *reinterpret_cast<const uint16_t*>(lds + __builtin_amdgcn_perm(q[2 * c + 1], lane_off, sel));
+                    v[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                }
+                *reinterpret_cast<uint32x4_t*>(wt + 16 * u) = v;
+            }
+        }
+    };
+
+    // MFMA role: wave (wr, wt) owns tile rows {64wr + 32j, 128 + 64wr + 32j}
+    // (gate/up) or 128wr + 32j (down), j < 2 / 4, and tokens 128wt + 32i
+    const int wr = wave & 1, wtk = wave >> 1;
+    int rbase[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        rbase[j] = NMAT == 2 ? (j < 2 ? 64 * wr + 32 * j : 128 + 64 * wr + 32 * (j - 2)) : 128 * wr + 32 * j;
+    float16_t acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+    const int l32 = lane & 31, lh = lane >> 5;
+    auto compute = [&](int st) {
+        const char* wt = lds + kStageOff[st];
+        const char* xt = wt + kTileB;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            half8_t av[4], bv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                av[j] = *reinterpret_cast<const half8_t*>(wt + (rbase[j] + l32) * kRowB + 32 * h + 16 * lh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bv[i] = *reinterpret_cast<const half8_t*>(xt + (128 * wtk + 32 * i + l32) * kRowB + 32 * h + 16 * lh);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[i], acc[j][i], 0, 0, 0);
+        }
+    };
+
+    __syncthreads();   // LUT tables complete
+    load(0, 0);
+    load(1, 1);
+    load(2, 2);
+    store(0, 0);
     __syncthreads();
+    for (int s = 0; s < ns; s += 6) {
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+            const int st = s + u;   // past ns (the last group's tail): loads read zeros, no MFMAs
+            load(u % 3, st + 3);               // into the slot step st left (stored last step)
+            store((u + 1) % 3, (u + 1) & 1);   // step st + 1, loaded two steps ago
+            if (st < ns) compute(u & 1);
+            __syncthreads();
+        }
+    }
+
+    // D lane layout: row 8 * (r / 4) + 4 * (lane / 32) + r % 4, token lane % 32
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tk = t0 + 128 * wtk + 32 * i + l32;
+        if (tk >= it.m) continue;
+        const size_t p = (size_t)(it.off + tk);
+#pragma unroll
+        for (int j = 0; j < (NMAT == 2 ? 2 : 4); ++j)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int row = r0 + (NMAT == 2 ? 64 * wr + 32 * j : 128 * wr + 32 * j) + 8 * q4 + 4 * lh;
+                if (row >= rows) continue;
+                if (NMAT == 2) {
+                    half4_t hv;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        hv[c] = (half_t)(silu_f32(acc[j][i][4 * q4 + c]) * acc[j + 2][i][4 * q4 + c]);
+                    *reinterpret_cast<half4_t*>(reinterpret_cast<half_t*>(a.out) + p * rows + row) = hv;
+                } else {
+                    float4_t fv;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) fv[c] = acc[j][i][4 * q4 + c];
+                    *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(a.out) + p * rows + row) = fv;
+                }
+            }
     }
 }
 
+template <int NMAT>
+__global__ __launch_bounds__(kThreadsTile) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void tile_kernel(GemmArgs a, int RT) {
+    __shared__ __attribute__((aligned(16))) char lds[kTileLds];
+    TileItem it;
+    if (!find_tile_item(a, RT, blockIdx.x, it)) return;   // uniform
+    switch (it.b) {
+        case 3: tile_item<NMAT, 3>(a, lds, it); break;
+        case 4: tile_item<NMAT, 4>(a, lds, it); break;
+        case 5: tile_item<NMAT, 5>(a, lds, it); break;
+        case 6: tile_item<NMAT, 6>(a, lds, it); break;
+        default: tile_item<NMAT, 16>(a, lds, it); break;
+    }
+}
+
+}  // namespace
+
 int launch_tile(const GemmArgs& a, hipStream_t s) {
-    const int S = a.T * a.k;
+    const long long S = (long long)a.T * a.k;
     if (S < a.mfma_min_tokens) return APMOE_OK;  // no group can reach the threshold
-    const int rows = a.stage == APMOE_GATE_UP_SWIGLU ? a.I : a.H;
-    const int mslots = (S + kBM - 1) / kBM + a.E;
-    dim3 grid((rows + kBN - 1) / kBN, mslots < 16 ? mslots : 16);
-    if (a.stage == APMOE_GATE_UP_SWIGLU)
-        hipLaunchKernelGGL(tile_simple_kernel<2>, grid, dim3(256), 0, s, a);
+    const bool gu = a.stage == APMOE_GATE_UP_SWIGLU;
+    const int mat_rows = gu ? 128 : 256;
+    const int RT = ((gu ? a.I : a.H) + mat_rows - 1) / mat_rows;
+    // token tiles: at most ceil(S / 256) plus one partial tile per group
+    const long long groups = std::min<long long>(a.E, S / a.mfma_min_tokens);
+    const long long items = ((S + kTToks - 1) / kTToks + groups) * RT;
+    if (items <= 0) return APMOE_OK;
+    if (gu)
+        hipLaunchKernelGGL(tile_kernel<2>, dim3((unsigned)items), dim3(kThreadsTile), 0, s, a, RT);
     else
-        hipLaunchKernelGGL(tile_simple_kernel<1>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(tile_kernel<1>, dim3((unsigned)items), dim3(kThreadsTile), 0, s, a, RT);
     return launch_status();
 }
 
