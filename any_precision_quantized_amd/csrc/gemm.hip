@@ -36,11 +36,14 @@ constexpr int kTRows = 256;              // weight rows per tile (gate/up: 128 +
 constexpr int kTToks = 256;              // tokens per tile
 constexpr int kRowB = 80;                // LDS bytes per tile row: 32 halves + 16 pad
 constexpr int kTileB = 256 * kRowB;
-// LDS map: LUT block 0 | W0 | X0 at 0, 16K, 36K; LUT block 1 | W1 | X1 at
-// 64K, 80K, 100K (the lookup permute puts the LUT block into address byte 2).
-constexpr int kStageOff[2] = {16384, 81920};
-constexpr int kTileLds = 81920 + 2 * kTileB;
+// LDS map: LUT block 0 at 0, stage 0 (W0 | X0) at 16K, LUT block 1 at 64K,
+// stages 1 and 2 at 80K and 120K (the lookup permute puts the LUT block into
+// address byte 2).  Three stages: step s uses stage s % 3, the same index as
+// its register slot, so the loop unrolls by three with no branch in its body.
+constexpr int kStageOff[3] = {16384, 81920, 81920 + 2 * kTileB};
+constexpr int kTileLds = 81920 + 4 * kTileB;
 static_assert(16384 + 2 * kTileB <= 65536, "stage 0 overlaps LUT block 1");
+static_assert(kTileLds <= 160 * 1024, "tile LDS exceeds 160 KiB");
 
 struct TileItem {
     int e, off, m, b, rt, tt;
@@ -169,8 +172,6 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
     auto store = [&](int r, int st) {   // decode into LDS stage st
         char* wt = lds + kStageOff[st] + tid * kRowB;
         char* xt = lds + kStageOff[st] + kTileB + tid * kRowB;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<half8_t*>(xt + 16 * j) = xreg[r][j];
         if constexpr (B == 16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -184,21 +185,25 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr) q[rr] = rr < B ? wreg[r][B - 1 - rr] : 0u;   // bit rr <- plane B-1-rr
             transpose_bytes<B>(q);
-            // byte u of q[j] is the code of column 8u + j: eight lookups, four
-            // packed dwords, one 16-byte store per byte lane
+            // byte u of q[j] is the code of column 8u + j.  All 32 lookups go
+            // out before any store: a store between them would be ordered
+            // before the later lookups (same LDS array), one round trip each.
+            uint32x4_t v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t sel = 0x0C020400u | ((uint32_t)u << 8);
-                uint32x4_t v;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const uint32_t lo = *reinterpret_cast<const uint16_t*>(lds + __builtin_amdgcn_perm(q[2 * c], lane_off, sel));
                     const uint32_t hi = *reinterpret_cast<const uint16_t*>(lds + __builtin_amdgcn_perm(q[2 * c + 1], lane_off, sel));
-                    v[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                    v[u][c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
-                *reinterpret_cast<uint32x4_t*>(wt + 16 * u) = v;
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) *reinterpret_cast<uint32x4_t*>(wt + 16 * u) = v[u];
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<half8_t*>(xt + 16 * j) = xreg[r][j];
     };
 
     // MFMA role: wave (wr, wt) owns tile rows {64wr + 32j, 128 + 64wr + 32j}
@@ -242,13 +247,19 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
     load(2, 2);
     store(0, 0);
     __syncthreads();
-    for (int s = 0; s < ns; s += 6) {
+    // Step st: refill the register slot step st left with step st + 3,
+    // multiply step st, decode step st + 1 (loaded two steps ago) into its
+    // stage.  No branch, so decode and MFMAs share one scheduling region, and
+    // the operand reads precede the stage writes in program order, so no
+    // assumed LDS alias holds the MFMAs behind the decode; steps past ns (at
+    // most two in the last group) read zeros and add nothing.
+    for (int s = 0; s < ns; s += 3) {
 #pragma unroll
-        for (int u = 0; u < 6; ++u) {
-            const int st = s + u;   // past ns (the last group's tail): loads read zeros, no MFMAs
-            load(u % 3, st + 3);               // into the slot step st left (stored last step)
-            store((u + 1) % 3, (u + 1) & 1);   // step st + 1, loaded two steps ago
-            if (st < ns) compute(u & 1);
+        for (int u = 0; u < 3; ++u) {
+            const int st = s + u;
+            load(u, st + 3);
+            compute(u);                        // its LDS reads come before the writes below
+            store((u + 1) % 3, (u + 1) % 3);
             __syncthreads();
         }
     }
