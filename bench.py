@@ -75,6 +75,35 @@ def cpu_baseline(inp, bits):
                       f"{dt:.1f} s; BLAS threads {threads} of {len(os.sched_getaffinity(0))} host cores"}
 
 
+def counted_traffic(kernel):
+    """HBM bytes per launch of `kernel` from a committed counter summary under
+    profiles/, or None when there is none or the kernel's sources changed since
+    the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                for key in ("traffic_kernel", "traffic_bytes_per_launch", "sources", "sources_sha256"):
+                    if line.startswith(key + ":"):
+                        fields[key] = line.split(":", 1)[1].strip()
+        if fields.get("traffic_kernel") != kernel or "sources" not in fields:
+            continue
+        h = hashlib.sha256()
+        try:
+            for src in fields["sources"].split():
+                with open(os.path.join(ROOT, src), "rb") as f:
+                    h.update(f.read())
+        except OSError:
+            return None
+        if h.hexdigest() == fields.get("sources_sha256"):
+            return float(fields["traffic_bytes_per_launch"])
+        return None
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +116,8 @@ def main():
                     help="run the shared expert on the main stream instead of the side stream")
     ap.add_argument("--replica-bytes", type=float, default=1.0e9,
                     help="weight bytes the rotating replicas must span (MALL defeat)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device five times (scale for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -105,6 +136,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return
     cfg = synth.get(args.workload)
     mfma_min = args.mfma_min_tokens or L.DEFAULT_MFMA_MIN_TOKENS
     inp = synth.make_inputs(cfg, seed=0)
@@ -253,7 +294,7 @@ def main():
         "hbm_frac": layer_gbs / HBM_PEAK_GBS,
         "expert_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(dominant),
                      "algorithmic_bytes": dom_bytes, "avg_us": dom_us},
         "per_launch_us": {n: round(per[n], 2) for n in names},
         "per_launch_bytes": {n: int(by.get(n, 0)) for n in names},
