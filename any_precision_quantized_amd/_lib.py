@@ -45,10 +45,10 @@ def _lib():
         sig = {
             "apmoe_route": [_vp, _c_int, _c_int, _vp, _vp, ctypes.c_float, _c_int, _c_int, _vp, _vp, _vp,
                             _c_size, _vp],
-            "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp],
+            "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp],
             "apmoe_bitplane_lut_gemm": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                         _c_int, _c_int, _c_int, _vp, _c_size, _vp],
-            "apmoe_combine": [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp],
+            "apmoe_combine": [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp],
             "apmoe_plan_bitwidths": [_c_int, _c_int, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp],
             "apmoe_commit_bits": [_vp, _c_int, _vp, _vp],
             "apmoe_workspace_bytes": [_c_int, _c_int, _c_int, _c_int, _c_int],
@@ -129,13 +129,15 @@ def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, ws=None, stream=N
     _check(rc, "apmoe_route")
 
 
-def permute(topk_ids, E, counts, offsets, sorted_slots, pos_of_slot, stream=None):
+def permute(topk_ids, E, counts, offsets, sorted_slots, pos_of_slot, n_shared=0, stream=None):
+    """Grouping over E + n_shared experts and T * (k + n_shared) slots (the
+    n_shared always-on experts first)."""
     torch = _torch()
     T, k = topk_ids.shape
-    S = T * k
-    rc = _lib().apmoe_permute(_ptr(topk_ids, torch.int32, S, "topk_ids"), T, k, E,
-                              _ptr(counts, torch.int32, E, "counts"),
-                              _ptr(offsets, torch.int32, E + 1, "offsets"),
+    S = T * (k + n_shared)
+    rc = _lib().apmoe_permute(_ptr(topk_ids, torch.int32, T * k, "topk_ids"), T, k, E, n_shared,
+                              _ptr(counts, torch.int32, E + n_shared, "counts"),
+                              _ptr(offsets, torch.int32, E + n_shared + 1, "offsets"),
                               _ptr(sorted_slots, torch.int32, S, "sorted_slots"),
                               _ptr(pos_of_slot, torch.int32, S, "pos_of_slot"), None, 0,
                               _stream(stream))
@@ -180,11 +182,12 @@ def bitplane_lut_gemm(stage, experts_desc, bits, E, offsets, sorted_slots, k, in
     _check(rc, "apmoe_bitplane_lut_gemm")
 
 
-def combine(Y, pos_of_slot, topk_w, T, k, H, y_shared, out, stream=None):
+def combine(Y, pos_of_slot, topk_w, T, k, H, y_shared, out, n_shared=0, stream=None):
     torch = _torch()
-    rc = _lib().apmoe_combine(_ptr(Y, torch.float32, T * k * H, "Y"),
-                              _ptr(pos_of_slot, torch.int32, T * k, "pos_of_slot"),
-                              _ptr(topk_w, torch.float32, T * k, "topk_w"), T, k, H,
+    kk = k + n_shared
+    rc = _lib().apmoe_combine(_ptr(Y, torch.float32, T * kk * H, "Y"),
+                              _ptr(pos_of_slot, torch.int32, T * kk, "pos_of_slot"),
+                              _ptr(topk_w, torch.float32, T * k, "topk_w"), T, k, n_shared, H,
                               _ptr(y_shared, torch.float32, T * H, "y_shared"),
                               _ptr(out, torch.float16, T * H, "out"), _stream(stream))
     _check(rc, "apmoe_combine")

@@ -3,22 +3,26 @@
 
 namespace apmoe {
 
-// out[t][h] = sum_j w[t][j] * Y[pos[t*k+j]][h] (+ y_shared[t][h]), fp32 in
-// ascending j, one rounding to fp16.  One thread per 4 consecutive h.
+// out[t][h] = sum_j w[t][j] * Y[pos[t*kk + nsh + j]][h]
+//           + sum_{j < nsh} Y[pos[t*kk + j]][h] (+ y_shared[t][h]), kk = k + nsh,
+// fp32 in that order (routed in ascending j, then the always-on parts), one
+// rounding to fp16.  One thread per 4 consecutive h.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       const int32_t* __restrict__ pos,
-                                                      const float* __restrict__ w, int T, int k,
+                                                      const float* __restrict__ w, int T, int k, int nsh,
                                                       int H, const float* __restrict__ ysh,
                                                       half_t* __restrict__ out) {
     const int t = blockIdx.y;
     const int h = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (t >= T || h >= H) return;
+    const size_t kk = (size_t)(k + nsh);
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
         const float g = w[(size_t)t * k + j];
-        const float4_t y = *reinterpret_cast<const float4_t*>(Y + (size_t)pos[(size_t)t * k + j] * H + h);
+        const float4_t y = *reinterpret_cast<const float4_t*>(Y + (size_t)pos[t * kk + nsh + j] * H + h);
         acc = acc + g * y;
     }
+    for (int j = 0; j < nsh; ++j) acc = acc + *reinterpret_cast<const float4_t*>(Y + (size_t)pos[t * kk + j] * H + h);
     if (ysh) acc = acc + *reinterpret_cast<const float4_t*>(ysh + (size_t)t * H + h);
     half4_t o = {(half_t)acc[0], (half_t)acc[1], (half_t)acc[2], (half_t)acc[3]};
     *reinterpret_cast<half4_t*>(out + (size_t)t * H + h) = o;
@@ -57,13 +61,13 @@ __global__ void commit_bits_kernel(BitsArg bits, int E, int8_t* __restrict__ dst
 using namespace apmoe;
 
 extern "C" int apmoe_combine(const float* Y, const int32_t* pos_of_slot, const float* topk_w, int T,
-                             int k, int H, const float* y_shared, uint16_t* out, void* stream) {
-    if (T < 0 || k < 1 || H <= 0 || H % 32) return APMOE_EINVAL;
+                             int k, int n_shared, int H, const float* y_shared, uint16_t* out, void* stream) {
+    if (T < 0 || k < 1 || n_shared < 0 || H <= 0 || H % 32) return APMOE_EINVAL;
     if (T == 0) return APMOE_OK;
     if (!Y || !pos_of_slot || !topk_w || !out) return APMOE_EINVAL;
     dim3 grid((H / 4 + 255) / 256, T);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, as_stream(stream), Y, pos_of_slot, topk_w,
-                       T, k, H, y_shared, reinterpret_cast<half_t*>(out));
+                       T, k, n_shared, H, y_shared, reinterpret_cast<half_t*>(out));
     return launch_status();
 }
 

@@ -182,9 +182,14 @@ __device__ __forceinline__ void store_result(const GemmArgs& a, const Shape& sh,
 template <int NMAT, int B, int TT>
 __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape& sh, const Item& it, const Mats& mv,
                                       int t0, int s0, int s1, int wave, int lane, bool live, int rowc) {
-    constexpr int D = 3;        // steps of weights in flight
-    constexpr int NB = D + 1;   // unroll: register ring of weights; even, so the
-                                // two activation buffers alternate with u
+    // Steps of weights in flight.  Plane words arrive as 4-byte-per-lane loads,
+    // which need many loads outstanding to keep HBM busy; a single token tile
+    // leaves the registers for a deep ring (the multi-tile variants set the
+    // kernel's register budget).  NB (the unroll) stays even so the two
+    // activation buffers alternate with u.
+    constexpr int D = (TT == 1 && B != 16) ? (NMAT == 2 ? 5 : 7) : 3;
+    constexpr int NB = D + 1;
+    static_assert(NB % 2 == 0, "the activation buffers alternate with u");
     const int tid = threadIdx.x;
     const int i = lane & 15, g = lane >> 4;
 
@@ -313,47 +318,64 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
                 for (int rr = 0; rr < 8; ++rr) qv[mat][rr] = rr < B ? w[mat][B - 1 - rr] : 0u;  // bit rr <- plane B-1-rr
                 transpose_bytes<B>(qv[mat]);
             }
+            // Every lookup of the step (four column groups, both matrices) is
+            // issued before the first MFMA that needs one, so the step pays one
+            // LDS round trip instead of one per column group.
+            if constexpr (TT == 1) {
+                uint32x4_t ev[4][NMAT], od[4][NMAT];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t sel = 0x0C020400u | ((uint32_t)q << 8);
-                if constexpr (TT == 1) {
-                    half8_t bx[TT], bo[TT];
-                    b_ops(slot, q, bx, bo);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t sel = 0x0C020400u | ((uint32_t)q << 8);
 #pragma unroll
-                    for (int mat = 0; mat < NMAT; ++mat) {
-                        uint32x4_t ev, od;
+                    for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
-                            ev[c] = *reinterpret_cast<const uint16_t*>(
+                            ev[q][mat][c] = *reinterpret_cast<const uint16_t*>(
                                 lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
-                            od[c] = *reinterpret_cast<const uint16_t*>(
+                            od[q][mat][c] = *reinterpret_cast<const uint16_t*>(
                                 lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
                         }
-                        const half8_t ae = __builtin_bit_cast(half8_t, ev), ao = __builtin_bit_cast(half8_t, od);
-                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bx[0], acc[mat][0], 0, 0, 0);
-                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bo[0], acc[mat][0], 0, 0, 0);
-                    }
-                } else {
-                    // several tiles: pack the pairs once (one permute per two
-                    // lookups) and run one MFMA per tile instead of two
-                    half8_t bx[TT];
-                    b_tiles(slot, q, bx);
+                }
+                half8_t bx[4][1], bo[4][1];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) b_ops(slot, q, bx[q], bo[q]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int mat = 0; mat < NMAT; ++mat) {
-                        uint32x4_t w;
+                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ev[q][mat]),
+                                                                             bx[q][0], acc[mat][0], 0, 0, 0);
+                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, od[q][mat]),
+                                                                             bo[q][0], acc[mat][0], 0, 0, 0);
+                    }
+            } else {
+                // several tiles: pack the pairs once (one permute per two
+                // lookups) and run one MFMA per tile instead of two
+                uint32x4_t w[4][NMAT];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t sel = 0x0C020400u | ((uint32_t)q << 8);
+#pragma unroll
+                    for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
                             const uint32_t lo = *reinterpret_cast<const uint16_t*>(
                                 lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
                             const uint32_t hi = *reinterpret_cast<const uint16_t*>(
                                 lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
-                            w[c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                            w[q][mat][c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                         }
-                        const half8_t aw = __builtin_bit_cast(half8_t, w);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    half8_t bx[TT];
+                    b_tiles(slot, q, bx);
+#pragma unroll
+                    for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
                         for (int tt = 0; tt < TT; ++tt)
-                            acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bx[tt], acc[mat][tt], 0, 0, 0);
-                    }
+                            acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, w[q][mat]),
+                                                                                  bx[tt], acc[mat][tt], 0, 0, 0);
                 }
             }
         };

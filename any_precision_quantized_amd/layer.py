@@ -6,6 +6,11 @@ per-call buffers and chains the C-ABI entry points:
 
     route -> permute -> gemm(GATE_UP_SWIGLU) -> gemm(DOWN) [-> shared expert] -> combine
 
+An fp16 shared expert whose intermediate size is n times the routed one runs
+inside the routed launches as n always-on experts (its gate/up row blocks and
+its down column blocks, placed first in the descriptor table); otherwise it
+runs as its own launches on a side stream.
+
 PyTorch only provides device memory and the HIP stream; every step runs in
 libapmoe's kernels.
 """
@@ -89,6 +94,31 @@ class ExpertTable:
                            for name, ent in d.items()})
         return ExpertTable(None, self.device, _tensors=copies)
 
+    @staticmethod
+    def concat(*tables: "ExpertTable") -> "ExpertTable":
+        """One descriptor array over the experts of several tables (no copies)."""
+        tensors = [d for t in tables for d in t.tensors]
+        return ExpertTable(None, tables[0].device, _tensors=tensors)
+
+    def split_rows(self, H: int, I: int) -> "ExpertTable":
+        """An fp16 single-expert table with intermediate size n*I as n experts of
+        size I: gate/up row blocks (views) and down column blocks (copied once
+        to contiguous [H, I])."""
+        assert self.E == 1
+        d = self.tensors[0]
+        g, u, dn = d["gate"]["w16"], d["up"]["w16"], d["down"]["w16"]
+        Is = g.numel() // H
+        assert Is % I == 0 and u.numel() == Is * H and dn.numel() == H * Is
+        g2, u2, d2 = g.view(Is, H), u.view(Is, H), dn.view(H, Is)
+        parts = []
+        for v in range(Is // I):
+            rows = slice(v * I, (v + 1) * I)
+            parts.append({"gate": {"planes": None, "luts": [None] * 4, "w16": g2[rows].reshape(-1)},
+                          "up": {"planes": None, "luts": [None] * 4, "w16": u2[rows].reshape(-1)},
+                          "down": {"planes": None, "luts": [None] * 4,
+                                   "w16": d2[:, rows].contiguous().reshape(-1)}})
+        return ExpertTable(None, self.device, _tensors=parts)
+
     def nbytes(self) -> int:
         n = 0
         for d in self.tensors:
@@ -114,23 +144,34 @@ class MoELayer:
         self.w_router = torch.as_tensor(np.ascontiguousarray(w_router), dtype=torch.float32).to(device)
         self.bias = None if bias is None else torch.as_tensor(np.ascontiguousarray(bias), dtype=torch.float32).to(device)
         self.experts = experts
-        self.bits = torch.zeros(E, dtype=torch.int8, **dev)
+        self.shared = shared
+        self.shared_I = shared_I
+        # always-on experts: the shared expert split into n of the routed size
+        self.n_shared = shared_I // I if (shared is not None and shared_I % I == 0) else 0
+        n = self.n_shared
+        E2, kk = E + n, k + n
+        self.E2, self.kk = E2, kk
+        self.bits = torch.zeros(E2, dtype=torch.int8, **dev)
+        if n:
+            _lib.commit_bits([16] * n, self.bits[:n])
+            self._tables = {}
+            self.table = self._fused(experts, shared)
+        else:
+            self.table = experts
         self.commit(bits)
-        S = T * k
+        S = T * kk
         self.topk_ids = torch.empty((T, k), dtype=torch.int32, **dev)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, **dev)
-        self.counts = torch.empty(E, dtype=torch.int32, **dev)
-        self.offsets = torch.empty(E + 1, dtype=torch.int32, **dev)
+        self.counts = torch.empty(E2, dtype=torch.int32, **dev)
+        self.offsets = torch.empty(E2 + 1, dtype=torch.int32, **dev)
         self.sorted_slots = torch.empty(S, dtype=torch.int32, **dev)
         self.pos_of_slot = torch.empty(S, dtype=torch.int32, **dev)
         self.A = torch.empty((S, I), dtype=torch.float16, **dev)
         self.Y = torch.empty((S, H), dtype=torch.float32, **dev)
         self.out = torch.empty((T, H), dtype=torch.float16, **dev)
-        nws = _lib.workspace_bytes(T, k, E, H, I)
+        nws = _lib.workspace_bytes(T, kk, E2, H, I)
         self.ws = torch.empty(nws, dtype=torch.uint8, **dev) if nws else None
-        self.shared = shared
-        self.shared_I = shared_I
-        if shared is not None:
+        if shared is not None and not n:
             # the shared expert runs on a side stream (default priority) with
             # its own workspace, overlapping routing and the routed experts
             self.side = torch.cuda.Stream(device=device)
@@ -144,17 +185,26 @@ class MoELayer:
             self.A_sh = torch.empty((T, shared_I), dtype=torch.float16, **dev)
             self.Y_sh = torch.empty((T, H), dtype=torch.float32, **dev)
 
+    def _fused(self, experts: ExpertTable, shared: ExpertTable) -> ExpertTable:
+        """Descriptor table [shared parts..., routed experts...] (cached per pair)."""
+        key = (id(experts), id(shared))
+        if key not in self._tables:
+            self._tables[key] = (ExpertTable.concat(shared.split_rows(self.H, self.I), experts), experts, shared)
+        return self._tables[key][0]
+
     def commit(self, bits):
-        _lib.commit_bits(bits, self.bits)
+        """Routed bitwidths (the always-on parts stay at 16)."""
+        _lib.commit_bits(bits, self.bits[self.n_shared:])
 
     def forward(self, x, experts: Optional[ExpertTable] = None, shared: Optional[ExpertTable] = None):
         """x: device fp16 [T, H].  Returns the fp16 output [T, H] (a buffer reused by later calls)."""
+        import torch
         ex = self.experts if experts is None else experts
         sh = self.shared if shared is None else shared
-        import torch
-        T, H, I, E, k = self.T, self.H, self.I, self.E, self.k
+        T, H, I, E, k, n = self.T, self.H, self.I, self.E, self.k, self.n_shared
+        side = sh is not None and not n
         ysh = None
-        if sh is not None:
+        if side:
             main = torch.cuda.current_stream()
             self.ev_fork.record(main)
             self.side.wait_event(self.ev_fork)
@@ -168,15 +218,17 @@ class MoELayer:
                                        self.ws_sh)
             self.ev_join.record(self.side)
             ysh = self.Y_sh
+        table = self._fused(ex, sh) if n else ex
+        E2, kk = self.E2, self.kk
         _lib.route(x, self.w_router, self.bias, self.logit_scale, k, self.topk_ids, self.topk_w, self.ws)
-        _lib.permute(self.topk_ids, E, self.counts, self.offsets, self.sorted_slots, self.pos_of_slot)
-        _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, ex.desc, self.bits, E, self.offsets, self.sorted_slots,
-                               k, x, self.A, T, H, I, self.mfma_min_tokens, self.ws)
-        _lib.bitplane_lut_gemm(_lib.DOWN, ex.desc, self.bits, E, self.offsets, self.sorted_slots,
-                               k, self.A, self.Y, T, H, I, self.mfma_min_tokens, self.ws)
-        if sh is not None:
+        _lib.permute(self.topk_ids, E, self.counts, self.offsets, self.sorted_slots, self.pos_of_slot, n)
+        _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, table.desc, self.bits, E2, self.offsets, self.sorted_slots,
+                               kk, x, self.A, T, H, I, self.mfma_min_tokens, self.ws)
+        _lib.bitplane_lut_gemm(_lib.DOWN, table.desc, self.bits, E2, self.offsets, self.sorted_slots,
+                               kk, self.A, self.Y, T, H, I, self.mfma_min_tokens, self.ws)
+        if side:
             torch.cuda.current_stream().wait_event(self.ev_join)
-        _lib.combine(self.Y, self.pos_of_slot, self.topk_w, T, k, H, ysh, self.out)
+        _lib.combine(self.Y, self.pos_of_slot, self.topk_w, T, k, H, ysh, self.out, n)
         return self.out
 
 

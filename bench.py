@@ -35,26 +35,31 @@ def expert_bytes(H, I, b):
     return 2 * (I * H * b // 8 + I * (1 << b) * 2), H * I * b // 8 + H * (1 << b) * 2
 
 
-def algorithmic(cfg, bits, counts, mfma_min):
+def algorithmic(cfg, bits, counts, mfma_min, n_shared=0):
     """Bytes each launch must move (planes of the top b bits + LUT_b, or fp16 rows,
-    plus activations in and out) and the expert flops."""
+    plus activations in and out) and the expert flops.  With n_shared > 0 the
+    shared expert runs as n always-on fp16 experts inside the stage launches
+    (counts then cover those n experts first, then the routed ones)."""
     H, I, T, k, E = cfg.H, cfg.I, cfg.T, cfg.k, cfg.E
+    kk = k + n_shared
     by = {"route": T * H * 2 + E * H * 4 + (E * 4 if cfg.router_bias else 0) + T * k * 8,
-          "permute": T * k * 4 + (2 * E + 1) * 4 + T * k * 8,
+          "permute": T * k * 4 + (2 * (E + n_shared) + 1) * 4 + T * kk * 8,
           "gate_up_gemv": 0, "gate_up_tile": 0, "down_gemv": 0, "down_tile": 0,
           "shared_gate_up": 0, "shared_down": 0,
-          "combine": T * k * (H * 4 + 8) + T * H * 2 + (T * H * 4 if cfg.shared_I else 0)}
+          "combine": T * kk * (H * 4 + 4) + T * k * 4 + T * H * 2
+          + (T * H * 4 if cfg.shared_I and not n_shared else 0)}
     flops = 0
-    for e in range(E):
+    all_bits = [16] * n_shared + [int(b) for b in bits]
+    for e in range(E + n_shared):
         m = int(counts[e])
         if m == 0:
             continue
-        wgu, wd = expert_bytes(H, I, int(bits[e]))
+        wgu, wd = expert_bytes(H, I, all_bits[e])
         path = "tile" if m >= mfma_min else "gemv"
         by["gate_up_" + path] += wgu + m * H * 2 + m * I * 2
         by["down_" + path] += wd + m * I * 2 + m * H * 4
         flops += 6 * m * H * I
-    if cfg.shared_I:
+    if cfg.shared_I and not n_shared:
         Is = cfg.shared_I
         by["shared_gate_up"] = 2 * Is * H * 2 + T * H * 2 + T * Is * 2
         by["shared_down"] = H * Is * 2 + T * Is * 2 + T * H * 4
@@ -162,7 +167,8 @@ def main():
     layer.forward(x)
     torch.cuda.synchronize()
     counts = layer.counts.cpu().numpy()
-    by, flops = algorithmic(cfg, bits, counts, mfma_min)
+    nsh = layer.n_shared
+    by, flops = algorithmic(cfg, bits, counts, mfma_min, nsh)
     step_bytes = sum(by.values())
     weight_bytes = sum(v for k_, v in by.items() if k_.startswith(("gate_up", "down", "shared")))
     R = max(2, math.ceil(args.replica_bytes / max(1, weight_bytes)))
@@ -171,7 +177,7 @@ def main():
 
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    side = getattr(layer, "side", None)           # the shared expert's stream
+    side = getattr(layer, "side", None)           # the shared expert's stream (when not fused)
     if args.serial_shared and side is not None:
         side = stream
     sp2 = side.cuda_stream if side is not None else None
@@ -185,8 +191,12 @@ def main():
 
     # Every launch of a step as (name, callable, stream) with its raw arguments
     # bound once; "fork"/"join" entries order the shared expert's side stream.
+    E2, kk = E + nsh, k + nsh
+
     def launches(r):
         tab, sh = tables[r], shared[r]
+        if nsh:
+            tab, sh = layer._fused(tab, sh), None   # shared parts run as always-on experts
         seq = []
         if sh is not None:
             Is = cfg.shared_I
@@ -201,20 +211,20 @@ def main():
         seq += [
             ("route", lambda: lib.apmoe_route(p(x), T, H, p(layer.w_router), p(layer.bias), layer.logit_scale,
                                               E, k, p(layer.topk_ids), p(layer.topk_w), ws, wsb, sp), stream),
-            ("permute", lambda: lib.apmoe_permute(p(layer.topk_ids), T, k, E, p(layer.counts), p(layer.offsets),
+            ("permute", lambda: lib.apmoe_permute(p(layer.topk_ids), T, k, E, nsh, p(layer.counts), p(layer.offsets),
                                                   p(layer.sorted_slots), p(layer.pos_of_slot), None, 0, sp), stream),
         ]
         for stage, name, src, dst in ((_lib.GATE_UP_SWIGLU, "gate_up", x, layer.A),
                                       (_lib.DOWN, "down", layer.A, layer.Y)):
             for flag, path in ((_lib.ONLY_GEMV, "gemv"), (_lib.ONLY_TILE, "tile")):
                 seq.append((f"{name}_{path}", (lambda st=stage | flag, s_=src, d_=dst: lib.apmoe_bitplane_lut_gemm(
-                    st, p(tab.desc), p(layer.bits), E, p(layer.offsets), p(layer.sorted_slots), k, p(s_), p(d_),
+                    st, p(tab.desc), p(layer.bits), E2, p(layer.offsets), p(layer.sorted_slots), kk, p(s_), p(d_),
                     T, H, I, mfma_min, ws, wsb, sp)), stream))
         ysh = p(layer.Y_sh) if sh is not None else None
         if sh is not None:
             seq.append(("join", None, None))
         seq.append(("combine", lambda: lib.apmoe_combine(p(layer.Y), p(layer.pos_of_slot), p(layer.topk_w), T, k,
-                                                          H, ysh, p(layer.out), sp), stream))
+                                                          nsh, H, ysh, p(layer.out), sp), stream))
         return seq
 
     steps = [launches(r) for r in range(R)]
@@ -289,7 +299,8 @@ def main():
                                + (f" + fp16 shared expert I{cfg.shared_I}" if cfg.shared_I else "")
                                + f", bits {dict(sorted((int(b), int((bits == b).sum())) for b in set(bits.tolist())))}",
                    "mfma_min_tokens": mfma_min, "weight_replicas": R,
-                   "groups": sorted([int(c) for c in counts if c > 0], reverse=True)},
+                   "shared_as_always_on_experts": nsh,
+                   "groups": sorted([int(c) for c in counts[nsh:] if c > 0], reverse=True)},
         "hbm_gbs": layer_gbs,
         "hbm_frac": layer_gbs / HBM_PEAK_GBS,
         "expert_tflops": flops / (ms_per_step * 1e-3) / 1e12,

@@ -100,16 +100,22 @@ int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const fl
 
 /*
  * Group slots by expert (stable: within an expert, slots in ascending order).
- *  counts[e]       number of slots routed to e                    int32 [E]
- *  offsets[e]      exclusive prefix sum of counts, offsets[E] = S int32 [E+1]
+ * Each token owns kk = k + n_shared slots.  n_shared >= 0 always-on experts
+ * (a shared expert split into n_shared experts of the routed size, each taking
+ * every token with weight 1) come first: slot t*kk + j is expert j for
+ * j < n_shared and expert n_shared + topk_ids[t][j - n_shared] otherwise, so
+ * the grouping covers E2 = E + n_shared experts and S = T*kk slots.
+ *  counts[e]       number of slots of expert e                    int32 [E2]
+ *  offsets[e]      exclusive prefix sum of counts, offsets[E2] = S int32 [E2+1]
  *  sorted_slots[p] slot at sorted position p                      int32 [S]
  *  pos_of_slot[s]  sorted position of slot s (inverse)            int32 [S]
- * Every topk_ids entry must lie in [0, E).  ws/ws_bytes: unused (pass NULL, 0);
- * kept so the call can grow a workspace without an ABI change.
+ * Every topk_ids entry must lie in [0, E); E2 <= APMOE_MAX_EXPERTS.
+ * ws/ws_bytes: unused (pass NULL, 0); kept so the call can grow a workspace
+ * without an ABI change.
  */
-int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
-                  int32_t* sorted_slots, int32_t* pos_of_slot, void* ws, size_t ws_bytes,
-                  void* stream);
+int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int n_shared, int32_t* counts,
+                  int32_t* offsets, int32_t* sorted_slots, int32_t* pos_of_slot, void* ws,
+                  size_t ws_bytes, void* stream);
 
 /*
  * One stage of every routed expert's FFN over its group of slots.
@@ -130,8 +136,11 @@ int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
  *           bytes (split-K partial sums; 0 for shapes that never split K).
  *           Calls that share one workspace must not overlap.
  * The dispatch reads counts and bitwidths on the device: no host sync.
- * An always-on shared expert is the same call with E = 1, bits = {16},
- * offsets = {0, T}, sorted_slots = 0..T-1 and k = 1.
+ * An always-on shared expert whose intermediate size is n times I runs in the
+ * same call as n extra fp16 experts (its gate/up row blocks and its down
+ * column blocks) grouped by apmoe_permute with n_shared = n (pass E + n and
+ * k + n here); any shared expert can also run alone as this call with E = 1,
+ * bits = {16}, offsets = {0, T}, sorted_slots = 0..T-1 and k = 1.
  */
 int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, const int8_t* bits, int E,
                             const int32_t* offsets, const int32_t* sorted_slots, int k,
@@ -139,12 +148,14 @@ int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, const int8_t
                             int mfma_min_tokens, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Weighted combine: out[t][h] = sum_{j=0..k-1} topk_w[t][j] * Y[pos_of_slot[t*k+j]][h]
- * (+ y_shared[t][h]), summed in fp32 in ascending j, rounded once to fp16.
- *  Y fp32 [S][H] (sorted order); y_shared fp32 [T][H] or NULL; out fp16 [T][H].
+ * Weighted combine, kk = k + n_shared slots per token (as apmoe_permute):
+ *   out[t][h] = sum_{j=0..k-1} topk_w[t][j] * Y[pos_of_slot[t*kk + n_shared + j]][h]
+ *             + sum_{j=0..n_shared-1} Y[pos_of_slot[t*kk + j]][h]  (+ y_shared[t][h]),
+ * summed in fp32 in that order, rounded once to fp16.
+ *  Y fp32 [T*kk][H] (sorted order); y_shared fp32 [T][H] or NULL; out fp16 [T][H].
  */
 int apmoe_combine(const float* Y, const int32_t* pos_of_slot, const float* topk_w, int T, int k,
-                  int H, const float* y_shared, uint16_t* out, void* stream);
+                  int n_shared, int H, const float* y_shared, uint16_t* out, void* stream);
 
 /*
  * Greedy bitwidth planner (host only, touches no GPU).  Starting from every

@@ -53,7 +53,28 @@ def run_layer(inp, bits, mfma_min_tokens=L.DEFAULT_MFMA_MIN_TOKENS, table=None, 
                counts=layer.counts.cpu().numpy(), offsets=layer.offsets.cpu().numpy(),
                sorted_slots=layer.sorted_slots.cpu().numpy(), pos_of_slot=layer.pos_of_slot.cpu().numpy(),
                A=layer.A.float().cpu().numpy(), Y=layer.Y.cpu().numpy(), out=out.float().cpu().numpy())
+    if layer.n_shared:
+        got = routed_view(got, layer.T, layer.k, layer.n_shared)
     return layer, got
+
+
+def routed_view(got, T, k, n):
+    """The grouping of a layer whose shared expert runs as n always-on experts
+    (experts 0..n-1, slots t*(k+n) + j for j < n), checked for those experts and
+    returned in the routed-only frame (experts 0..E-1, slots t*k + j)."""
+    kk = k + n
+    counts, offsets, ss, pos = got["counts"], got["offsets"], got["sorted_slots"], got["pos_of_slot"]
+    assert counts[:n].tolist() == [T] * n, "every token reaches every always-on expert once"
+    for v in range(n):
+        assert np.array_equal(ss[v * T:(v + 1) * T], np.arange(T) * kk + v), "always-on slots in token order"
+    base = n * T
+    rs = ss[base:]
+    slot = (rs // kk) * k + (rs % kk - n)
+    routed_pos = pos.reshape(T, kk)[:, n:].reshape(-1) - base
+    out = dict(got)
+    out.update(counts=counts[n:], offsets=offsets[n:] - base, sorted_slots=slot.astype(ss.dtype),
+               pos_of_slot=routed_pos.astype(pos.dtype), A=got["A"][base:], Y=got["Y"][base:])
+    return out
 
 
 def check_route(inp, got, ref_ids, ref_gates, ref_logits):

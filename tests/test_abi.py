@@ -49,9 +49,11 @@ def test_validation_before_launch():
     assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None, 0, None) == _lib.OK   # T = 0
     assert _lib.workspace_bytes(4, 2, 8, 64, 64) >= 4 * 8 * 8
     # permute
-    assert lib.apmoe_permute(fake, 4, 0, 8, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
-    assert lib.apmoe_permute(None, 4, 2, 8, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
-    assert lib.apmoe_permute(None, 0, 2, 8, None, None, None, None, None, 0, None) == _lib.OK
+    assert lib.apmoe_permute(fake, 4, 0, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(None, 4, 2, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(fake, 4, 2, 8, -1, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(fake, 4, 2, 250, 7, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL   # E + n > 256
+    assert lib.apmoe_permute(None, 0, 2, 8, 0, None, None, None, None, None, 0, None) == _lib.OK
     # gemm: bad stage, H or I not a multiple of 32, mfma_min_tokens < 1
     g = lib.apmoe_bitplane_lut_gemm
     assert g(7, fake, fake, 8, fake, fake, 2, fake, fake, 4, 64, 64, 16, None, 0, None) == _lib.EINVAL
@@ -61,8 +63,9 @@ def test_validation_before_launch():
     assert g(0, fake, fake, 8, fake, None, 2, fake, fake, 4, 64, 64, 16, None, 0, None) == _lib.EINVAL
     assert g(0, None, None, 8, None, None, 2, None, None, 0, 64, 64, 16, None, 0, None) == _lib.OK
     # combine
-    assert lib.apmoe_combine(fake, fake, fake, 4, 2, 48, None, fake, None) == _lib.EINVAL
-    assert lib.apmoe_combine(None, fake, fake, 4, 2, 64, None, fake, None) == _lib.EINVAL
+    assert lib.apmoe_combine(fake, fake, fake, 4, 2, 0, 48, None, fake, None) == _lib.EINVAL
+    assert lib.apmoe_combine(None, fake, fake, 4, 2, 0, 64, None, fake, None) == _lib.EINVAL
+    assert lib.apmoe_combine(fake, fake, fake, 4, 2, -1, 64, None, fake, None) == _lib.EINVAL
     # pack: rows not a multiple of 16, cols not a multiple of 32, overlap
     assert lib.apmoe_pack_planes(fake, 24, 64, ctypes.c_void_p(0x100000), None) == _lib.EINVAL
     assert lib.apmoe_pack_planes(fake, 32, 48, ctypes.c_void_p(0x100000), None) == _lib.EINVAL

@@ -35,6 +35,10 @@ SMALL = {
     "t1": synth.custom("t1", E=8, H=512, I=384, k=2, T=1, bits=(3, 4, 5, 6, 16, 3, 4, 5)),
     # 128 tokens over 3 experts: groups of ~85 (several 64-token tiles, ragged)
     "wide": synth.custom("wide", E=3, H=192, I=288, k=2, T=128, bits=(4, 6, 3)),
+    # shared expert of 3x the routed size: three always-on experts in the routed launches
+    "shared_fused": synth.custom("shared_fused", E=5, H=192, I=96, k=2, T=40, bits=(3, 4, 5, 6, 16), shared_I=288),
+    # shared expert whose size is no multiple of I: its own launches on a side stream
+    "shared_side": synth.custom("shared_side", E=4, H=160, I=128, k=1, T=33, bits=(6, 3, 4, 5), shared_I=224),
 }
 
 
