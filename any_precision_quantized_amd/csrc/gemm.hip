@@ -5,6 +5,7 @@
 // count and bitwidth and leaves at once when the group is empty or belongs to
 // the other path, so no count ever travels to the host.
 #include <algorithm>
+#include <climits>
 
 #include "common.hpp"
 #include "decode.hpp"
@@ -311,7 +312,7 @@ void tile_kernel(GemmArgs a, int RT) {
 
 int launch_tile(const GemmArgs& a, hipStream_t s) {
     const long long S = (long long)a.T * a.k;
-    if (S < a.mfma_min_tokens) return APMOE_OK;  // no group can reach the threshold
+    if (S < a.mfma_min_tokens || a.mfma_min_tokens == INT_MAX) return APMOE_OK;  // no group can reach it
     const bool gu = a.stage == APMOE_GATE_UP_SWIGLU;
     const int mat_rows = gu ? 128 : 256;
     const int RT = ((gu ? a.I : a.H) + mat_rows - 1) / mat_rows;
@@ -345,7 +346,12 @@ extern "C" int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, c
     if (!experts || !bits || !offsets || !in || !out) return APMOE_EINVAL;
     if (stage == APMOE_GATE_UP_SWIGLU && !sorted_slots) return APMOE_EINVAL;
     if (ws_bytes < apmoe_workspace_bytes(T, k, E, H, I)) return APMOE_ENOSPACE;
-    GemmArgs a{stage, experts, bits, E, offsets, sorted_slots, k, in, out, T, H, I, mfma_min_tokens};
+    // A token holds at most one slot of each expert, so no group exceeds T
+    // slots: below the threshold every group takes the GEMV path and the tile
+    // launch is skipped (the effective threshold keeps that true for any
+    // grouping the caller passes).
+    const int eff_min = T < mfma_min_tokens ? INT_MAX : mfma_min_tokens;
+    GemmArgs a{stage, experts, bits, E, offsets, sorted_slots, k, in, out, T, H, I, eff_min};
     hipStream_t s = as_stream(stream);
     if (paths != APMOE_ONLY_TILE) {
         const int rc = launch_gemv(a, ws, ws_bytes, s);

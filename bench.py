@@ -216,7 +216,9 @@ def main():
         ]
         for stage, name, src, dst in ((_lib.GATE_UP_SWIGLU, "gate_up", x, layer.A),
                                       (_lib.DOWN, "down", layer.A, layer.Y)):
-            for flag, path in ((_lib.ONLY_GEMV, "gemv"), (_lib.ONLY_TILE, "tile")):
+            # below T = mfma_min_tokens the library launches no tile kernel
+            paths = ((_lib.ONLY_GEMV, "gemv"),) + (((_lib.ONLY_TILE, "tile"),) if T >= mfma_min else ())
+            for flag, path in paths:
                 seq.append((f"{name}_{path}", (lambda st=stage | flag, s_=src, d_=dst: lib.apmoe_bitplane_lut_gemm(
                     st, p(tab.desc), p(layer.bits), E2, p(layer.offsets), p(layer.sorted_slots), kk, p(s_), p(d_),
                     T, H, I, mfma_min, ws, wsb, sp)), stream))

@@ -132,6 +132,9 @@ int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int n_shared, in
  *  mfma_min_tokens  groups with at least this many slots take the dequantise-
  *           to-LDS + MFMA tile path, smaller ones the bit-plane GEMV path
  *           (both paths give results within the same tolerance).  >= 1.
+ *           A token holds at most one slot of each expert, so when
+ *           T < mfma_min_tokens every group takes the GEMV path and no tile
+ *           kernel is launched.
  *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I)
  *           bytes (split-K partial sums; 0 for shapes that never split K).
  *           Calls that share one workspace must not overlap.
