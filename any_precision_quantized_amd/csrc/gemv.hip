@@ -1,45 +1,57 @@
 // Bit-plane + LUT GEMV path of apmoe_bitplane_lut_gemm: expert groups smaller
 // than mfma_min_tokens (decode-sized groups).
 //
-// Layout of the work (gfx950, wave64, v_mfma_f32_16x16x32_f16):
-//   D[row][token] = sum_k W[row][k] * X[token][k]
+// Layout of the work (gfx950, wave64), D[row][token] = sum_k W[row][k] X[token][k]:
+//
+// Bit-plane experts with at most 32 tokens (the decode case), with
+// v_mfma_f32_32x32x16_f16 on 32-row blocks:
+//   A operand (W): lane l holds row l % 32 of its wave pair's block and eight
+//                  consecutive columns of the plane word it decodes; waves
+//                  2p and 2p + 1 share rows 32p..32p+31 and split each K step
+//                  (128 columns = 4 words): wave parity h takes words 2h and
+//                  2h + 1, lane l word 2h + l / 32.
+//   B operand (X): lane l holds token l % 32 at the same eight columns.
+//   D:             lane l holds rows 8*(r/4) + 4*(l/32) + r%4 (r = 0..15) of
+//                  token l % 32; the pair adds its two halves at the end.
+// Other groups (fp16 rows, or more than 32 tokens), with
+// v_mfma_f32_16x16x32_f16 on 16-row blocks:
 //   A operand (W): lane l holds row (l % 16) of the wave's 16-row block and
 //                  the eight consecutive columns 8*q + 0..7 of the 32-column
 //                  word that lane group g = l / 16 owns in this K step
-//                  (a step is 128 columns; q = 0..3 picks one of the four
-//                  MFMAs a word feeds).
+//                  (q = 0..3 picks one of the four MFMAs a word feeds).
 //   B operand (X): lane l holds token (l % 16) of a 16-token tile at the
-//                  same eight columns, read from LDS.
+//                  same eight columns.
 //   D:             lane l holds rows 4*g + 0..3 for token l % 16.
-// One decoded A operand feeds up to four 16-token tiles.
+//   One decoded A operand feeds up to four 16-token tiles.
 //
-// A workgroup is four waves on four consecutive 16-row blocks of one expert
-// (one item: expert, 64-row block, K split), so the four waves read the same
+// A workgroup is four waves on 64 consecutive rows of one expert (one item:
+// expert, 64-row block, K split), so the four waves read the same
 // activations: the workgroup stages each K step's activation tiles in LDS
-// once (double-buffered, one barrier per step) and every wave reads its B
-// operands from there.  The grid holds one workgroup per possible item and
-// is not persistent: the hardware dispatcher hands items to free CUs, which
-// balances items of very different cost (3..6-bit or fp16 rows, 1..4 tiles).
+// once (double-buffered, one barrier per step; 16-byte chunks XOR-swizzled by
+// token row, so neither the stores nor the operand reads conflict) and every
+// wave reads its B operands from there.  LDS holds 48 KB and the kernel 168
+// VGPRs, so three workgroups share a CU.  The grid holds one workgroup per
+// possible item and is not persistent: the hardware dispatcher hands items to
+// free CUs, which balances items of very different cost (3..6-bit or fp16
+// rows, 1..4 tiles).
 //
 // Decode of one lane's word (32 columns of one row, b planes):
 //   * the plane words come from the packed layout: one 256-byte run per plane
 //     and 16-row group per step, so every load uses whole cache lines, and
-//     they are issued three steps ahead into a register ring;
+//     they are issued several steps ahead into a register ring;
 //   * the b plane words are bit-transposed in registers with delta swaps,
 //     giving eight registers R_s whose byte u is the b-bit code of column
 //     8*u + s (an 8x8 bit transpose per byte lane; the swaps of distance 1
 //     and 2 run first, while the planes past b are still zero words, so
 //     they cost nothing);
-//   * each wave stages the LUTs of its rows in LDS as table[code] rows of 256
-//     bytes shared by a pair of waves, the wave's 128-byte half holding 32
-//     dword slots, slot = 16*(g % 2) + row, so the 32 lanes of a half-wave read
-//     32 different banks whatever the codes; for gate/up the gate entry is the
-//     low and the up entry the high half of a slot.  A lookup address is
-//     pair * 64K + code * 256 + 128 * (wave % 2) + 4 * (lane % 32), built with
-//     one byte permute;
-//   * lookups return a weight in the low half of a dword; the even columns of
-//     a group feed one MFMA, the odd columns a second against activations
-//     shifted down one half, so no instruction packs pairs of halves.
+//   * each wave stages the LUTs of its 16 rows in LDS: the entry of code c for
+//     row r of wave w sits at c * 256 + 64 * w + 4 * r, gate in the low and up
+//     in the high half of the dword.  A lookup address (code in byte 1, the
+//     lane's row slot in byte 0) takes one byte permute.  On the 32-row path
+//     the 32 lanes of a half-wave hold 32 different rows, so they hit 32
+//     different banks whatever the codes;
+//   * a second permute packs each pair of looked-up halves into an operand
+//     dword, and every lookup of a step is issued before its first MFMA.
 // Only the top b planes of a b-bit expert are read.
 //
 // When the host splits K (only when the items of the possible experts would
@@ -56,14 +68,14 @@ constexpr int kWaves = 4;                    // 16-row blocks per item
 constexpr int kThreads = kWaves * kWave;
 constexpr int kItemRows = 16 * kWaves;
 constexpr int kMaxTiles = 4;                 // 16-token tiles per pass
-constexpr int kXRow = 272;                   // bytes per token row of a tile (128 halves + 16 pad)
+constexpr int kXRow = 256;                   // bytes per token row of a tile (128 halves)
 constexpr int kXTile = 16 * kXRow;
-// LDS: LUT block of waves 0/1 at 0, activation ring at 16K, LUT block of
-// waves 2/3 at 64K (the permute puts the block index into address byte 2).
-constexpr int kLutBlock = 64 * 256;          // 2^6 codes x 256 bytes
-constexpr int kXRing = kLutBlock;
-constexpr int kLdsBytes = 65536 + kLutBlock;
-static_assert(kXRing + 2 * kMaxTiles * kXTile <= 65536, "activation ring overlaps the second LUT block");
+// LDS: the four waves' LUTs at 0 (2^6 codes x 4 waves x 16 rows x 4 bytes),
+// then the double-buffered activation ring: 48 KB, three workgroups per CU.
+constexpr int kLutBytes = 64 * 256;
+constexpr int kXRing = kLutBytes;
+constexpr int kLdsBytes = kXRing + 2 * kMaxTiles * kXTile;
+static_assert(kLdsBytes <= 48 * 1024, "three workgroups per CU");
 constexpr int kTargetGroups = 1024;          // 256 CUs x 2 resident workgroups, twice over
 
 // Weight sources of one item.  Buffer resources are rebuilt per load group
@@ -126,18 +138,18 @@ __device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, in
     return false;
 }
 
-// Stage the LUTs of this wave's 16 rows: code v's 128-byte half row holds
-// the entry of row (slot % 16) in slots slot and slot + 16; gate in the low
-// and up in the high half of each dword.  Lanes cover 32 slots x 2 codes per
-// store, so each half-wave writes one whole half row (no bank conflicts).
+// Stage the LUTs of this wave's 16 rows: the entry of code v for row r sits
+// at v * 256 + 64 * wave + 4 * r (tab points at 64 * wave), gate in the low
+// and up in the high half of the dword.  Lane (r = lane % 16, p = lane / 16)
+// writes codes v0 + 2p and v0 + 2p + 1.
 template <int NMAT, int B>
 __device__ __forceinline__ void stage_luts(char* tab, const Mats& mv, int rowc, int lane) {
     constexpr int nent = 1 << B;
-    const int sl = lane & 31;
-    const int row = rowc + (sl & 15);
+    const int sl = lane & 15;
+    const int row = rowc + sl;
 #pragma unroll
-    for (int v0 = 0; v0 < nent; v0 += 4) {
-        const int v = v0 + 2 * (lane >> 5);
+    for (int v0 = 0; v0 < nent; v0 += 8) {
+        const int v = v0 + 2 * (lane >> 4);
         const uint32_t g = mv.lut[0][(row * nent + v) >> 1];
         uint32_t e0 = g & 0xFFFFu, e1 = g >> 16;
         if (NMAT == 2) {
@@ -179,15 +191,23 @@ __device__ __forceinline__ void store_result(const GemmArgs& a, const Shape& sh,
 // steps ahead and the weight loads D steps ahead, run this step's MFMAs
 // (B operands from the LDS tile), write the next step's activation tile
 // (loaded a step earlier), barrier.
-template <int NMAT, int B, int TT>
+//
+// W32 (bit-plane experts, at most 32 tokens): v_mfma_f32_32x32x16_f16 on
+// 32-row blocks.  Waves 2p and 2p + 1 share rows 32p..32p+31 of the item and
+// split every step's columns (wave parity h takes words 2h, 2h + 1; lane l
+// holds row l % 32 and word 2h + l / 32), so the 32 lanes of a half-wave read
+// 32 different rows' LUT slots: the lookups are free of bank conflicts with
+// one table copy.  The pair adds its two halves at the end.
+template <int NMAT, int B, int TT, bool W32 = false>
 __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape& sh, const Item& it, const Mats& mv,
                                       int t0, int s0, int s1, int wave, int lane, bool live, int rowc) {
-    // Steps of weights in flight.  Plane words arrive as 4-byte-per-lane loads,
-    // which need many loads outstanding to keep HBM busy; a single token tile
-    // leaves the registers for a deep ring (the multi-tile variants set the
-    // kernel's register budget).  NB (the unroll) stays even so the two
-    // activation buffers alternate with u.
-    constexpr int D = (TT == 1 && B != 16) ? (NMAT == 2 ? 5 : 7) : 3;
+    // Steps of weights in flight, within the 168-register budget: deeper for
+    // the small-tile variants, which hold the fewest accumulators and operand
+    // registers (measured on the decode shapes).  NB (the unroll) stays even
+    // so the two activation buffers alternate with u.
+    constexpr int D = B == 16 ? (NMAT == 2 ? (TT == 1 ? 3 : 1) : 3)
+                              : ((TT == 1 || W32) ? (NMAT == 2 ? 3 : 5) : (TT == 2 ? 3 : 1));
+    static_assert(!W32 || (B != 16 && TT <= 2), "W32 covers bit-plane experts with up to 32 tokens");
     constexpr int NB = D + 1;
     static_assert(NB % 2 == 0, "the activation buffers alternate with u");
     const int tid = threadIdx.x;
@@ -217,35 +237,31 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
             x[j] = buf_load_h8(r, (xok[j] && col < sh.K) ? xrow[j] + 2u * (uint32_t)col : kOutOfRange);
     };
     auto x_store = [&](const half8_t (&x)[TT], int slot) {
-        char* p = ring + slot * (TT * kXTile) + xn * kXRow + 16 * xc;
+        char* p = ring + slot * (TT * kXTile) + xn * kXRow + 16 * (xc ^ xn);   // chunk c of row n at c ^ n
 #pragma unroll
         for (int j = 0; j < TT; ++j) *reinterpret_cast<half8_t*>(p + j * kXTile) = x[j];
     };
 
     float4_t acc[NMAT][TT];
+    float16_t acc32[NMAT];
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
+    for (int mat = 0; mat < NMAT; ++mat) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) acc[mat][tt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc32[mat][r] = 0.f;
+    }
+    // W32: row block of the wave pair, word half, token row of the B operand
+    const int hp = wave & 1, rowc32 = rowc - 16 * hp;
+    const int n32 = lane & 31, h32 = lane >> 5;
+    const int nn = TT == 1 ? (n32 & 15) : n32;   // tokens past the staged tile read a staged row
 
     // B operands of column group q from a ring slot (lane group g holds the
-    // columns 32g + 8q + 0..7 of the step)
+    // columns 32g + 8q + 0..7 of the step: chunk 4g + q of row i)
     auto b_tiles = [&](int slot, int q, half8_t (&bx)[TT]) {
-        const char* p = ring + slot * (TT * kXTile) + i * kXRow + 64 * g + 16 * q;
+        const char* p = ring + slot * (TT * kXTile) + i * kXRow + 16 * ((4 * g + q) ^ i);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) bx[tt] = *reinterpret_cast<const half8_t*>(p + tt * kXTile);
-    };
-    // ... and with their odd halves moved down one half (upper halves zero)
-    auto b_ops = [&](int slot, int q, half8_t (&bx)[TT], half8_t (&bo)[TT]) {
-        const char* p = ring + slot * (TT * kXTile) + i * kXRow + 64 * g + 16 * q;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            bx[tt] = *reinterpret_cast<const half8_t*>(p + tt * kXTile);
-            uint32x4_t u = __builtin_bit_cast(uint32x4_t, bx[tt]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) u[c] >>= 16;
-            bo[tt] = __builtin_bit_cast(half8_t, u);
-        }
     };
 
     if constexpr (B == 16) {
@@ -267,7 +283,7 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 half8_t bx[TT];
-                const char* p = ring + slot * (TT * kXTile) + i * kXRow + 64 * q + 16 * g;
+                const char* p = ring + slot * (TT * kXTile) + i * kXRow + 16 * ((4 * q + g) ^ i);
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt) bx[tt] = *reinterpret_cast<const half8_t*>(p + tt * kXTile);
 #pragma unroll
@@ -297,10 +313,12 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
     } else {
         uint32_t pw[NB][NMAT][B];
         const uint32_t slab = (uint32_t)sh.rows * 16u * (uint32_t)sh.nsteps;   // bytes per plane
-        const uint32_t rg = (uint32_t)(rowc >> 4);
+        // the lane's word of each plane: row group, word within the step's run
+        const uint32_t rg = W32 ? (uint32_t)((rowc32 >> 4) + (n32 >> 4)) : (uint32_t)(rowc >> 4);
+        const uint32_t lw = W32 ? 64u * (uint32_t)(2 * hp + h32) + 4u * (uint32_t)(n32 & 15) : 4u * (uint32_t)lane;
         auto p_load = [&](uint32_t (&w)[NMAT][B], int s) {   // idle waves and steps past s1 read zeros
             const uint32_t n = (live && s < s1) ? mv.pbytes : 0u;
-            const uint32_t at = (rg * (uint32_t)sh.nsteps + (uint32_t)min(s, sh.nsteps - 1)) * 256u + 4u * lane;
+            const uint32_t at = (rg * (uint32_t)sh.nsteps + (uint32_t)min(s, sh.nsteps - 1)) * 256u + lw;
 #pragma unroll
             for (int mat = 0; mat < NMAT; ++mat) {
                 const __amdgpu_buffer_rsrc_t r = make_rsrc(mv.planes[mat], n);
@@ -308,8 +326,10 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
                 for (int p = 0; p < B; ++p) w[mat][p] = buf_load_u32(r, at, p * slab);
             }
         };
-        // lookup address: byte 0 = lane slot offset, byte 1 = code, byte 2 = LUT block
-        const uint32_t lane_off = ((uint32_t)(wave >> 1) << 16) | ((uint32_t)(wave & 1) << 7) | (4u * (lane & 31));
+        // lookup address: byte 0 = the lane's row slot, byte 1 = code (the
+        // pair's 32 rows are the two waves' 16-row tables, side by side)
+        const uint32_t lane_off = W32 ? (((uint32_t)(wave >> 1) << 7) | (4u * (uint32_t)n32))
+                                      : (((uint32_t)wave << 6) | (4u * (lane & 15)));
         auto compute = [&](const uint32_t (&w)[NMAT][B], int slot) {
             uint32_t qv[NMAT][8];
 #pragma unroll
@@ -320,41 +340,13 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
             }
             // Every lookup of the step (four column groups, both matrices) is
             // issued before the first MFMA that needs one, so the step pays one
-            // LDS round trip instead of one per column group.
-            if constexpr (TT == 1) {
-                uint32x4_t ev[4][NMAT], od[4][NMAT];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t sel = 0x0C020400u | ((uint32_t)q << 8);
-#pragma unroll
-                    for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            ev[q][mat][c] = *reinterpret_cast<const uint16_t*>(
-                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
-                            od[q][mat][c] = *reinterpret_cast<const uint16_t*>(
-                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
-                        }
-                }
-                half8_t bx[4][1], bo[4][1];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) b_ops(slot, q, bx[q], bo[q]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int mat = 0; mat < NMAT; ++mat) {
-                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ev[q][mat]),
-                                                                             bx[q][0], acc[mat][0], 0, 0, 0);
-                        acc[mat][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, od[q][mat]),
-                                                                             bo[q][0], acc[mat][0], 0, 0, 0);
-                    }
-            } else {
-                // several tiles: pack the pairs once (one permute per two
-                // lookups) and run one MFMA per tile instead of two
+            // LDS round trip instead of one per column group; a permute packs
+            // each pair of looked-up halves into one operand dword.
+            {
                 uint32x4_t w[4][NMAT];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint32_t sel = 0x0C020400u | ((uint32_t)q << 8);
+                    const uint32_t sel = 0x0C0C0400u | ((uint32_t)q << 8);
 #pragma unroll
                     for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
@@ -366,16 +358,30 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
                             w[q][mat][c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                         }
                 }
+                if constexpr (W32) {
+                    // B operand: token nn, columns 32 (2 hp + h32) + 8q + 0..7
+                    const char* xb = ring + slot * (TT * kXTile) + (nn >> 4) * kXTile + (nn & 15) * kXRow;
+                    const int cb = 4 * (2 * hp + h32);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    half8_t bx[TT];
-                    b_tiles(slot, q, bx);
+                    for (int q = 0; q < 4; ++q) {
+                        const half8_t bx = *reinterpret_cast<const half8_t*>(xb + 16 * ((cb + q) ^ (nn & 15)));
 #pragma unroll
-                    for (int mat = 0; mat < NMAT; ++mat)
+                        for (int mat = 0; mat < NMAT; ++mat)
+                            acc32[mat] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, w[q][mat]),
+                                                                                bx, acc32[mat], 0, 0, 0);
+                    }
+                } else {
 #pragma unroll
-                        for (int tt = 0; tt < TT; ++tt)
-                            acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, w[q][mat]),
-                                                                                  bx[tt], acc[mat][tt], 0, 0, 0);
+                    for (int q = 0; q < 4; ++q) {
+                        half8_t bx[TT];
+                        b_tiles(slot, q, bx);
+#pragma unroll
+                        for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                            for (int tt = 0; tt < TT; ++tt)
+                                acc[mat][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    __builtin_bit_cast(half8_t, w[q][mat]), bx[tt], acc[mat][tt], 0, 0, 0);
+                    }
                 }
             }
         };
@@ -398,7 +404,32 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
         }
     }
 
-    if (live) {
+    if constexpr (W32) {
+        // The odd wave of each pair hands its sums to the even one through
+        // LDS ([pair][mat][element][lane]); the even wave adds them (its half
+        // first) and stores rows 8 (r / 4) + 4 h32 + r % 4 for token n32.
+        __syncthreads();   // the ring is free
+        float* red = reinterpret_cast<float*>(ring) + (wave >> 1) * (NMAT * 16 * kWave);
+        if (hp) {
+#pragma unroll
+            for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[(mat * 16 + r) * kWave + lane] = acc32[mat][r];
+        }
+        __syncthreads();
+        if (!hp && live) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                float4_t s[NMAT];
+#pragma unroll
+                for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        s[mat][c] = acc32[mat][4 * rr + c] + red[(mat * 16 + 4 * rr + c) * kWave + lane];
+                store_result<NMAT>(a, sh, it, rowc32 + 8 * rr + 4 * h32, t0 + n32, s);
+            }
+        }
+    } else if (live) {
         const int row = rowc + 4 * g;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
@@ -420,7 +451,16 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, char* lds, const Sha
     const int s0 = min(sh.nsteps, it.ks * per), s1 = min(sh.nsteps, s0 + per);
     if (s0 >= s1) return;   // uniform over the workgroup
     if constexpr (B != 16) {
-        if (live) stage_luts<NMAT, B>(lds + (wave >> 1) * 65536 + (wave & 1) * 128, mv, rowc, lane);
+        if (live) stage_luts<NMAT, B>(lds + 64 * wave, mv, rowc, lane);
+    }
+    if constexpr (B != 16) {
+        if (it.m <= 32) {   // one pass of 32-row MFMA blocks
+            if (it.m > 16)
+                kpass<NMAT, B, 2, true>(a, lds, sh, it, mv, 0, s0, s1, wave, lane, live, rowc);
+            else
+                kpass<NMAT, B, 1, true>(a, lds, sh, it, mv, 0, s0, s1, wave, lane, live, rowc);
+            return;
+        }
     }
     for (int t0 = 0; t0 < it.m; t0 += 16 * kMaxTiles) {
         const int left = it.m - t0;
@@ -435,7 +475,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, char* lds, const Sha
 }
 
 template <int NMAT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gemv_kernel(GemmArgs a, int KS, float* partial) {
     __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
