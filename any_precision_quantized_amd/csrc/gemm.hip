@@ -6,6 +6,7 @@
 // the other path, so no count ever travels to the host.
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "common.hpp"
 #include "decode.hpp"
@@ -19,12 +20,14 @@ namespace apmoe {
 //   D[row][token] = sum_k W[row][k] * X[token][k]
 // Workgroup tile: 256 weight rows x 256 tokens, K step 32 (one plane word
 // per row).  For gate/up the 256 rows are 128 gate rows and the same 128 up
-// rows, so the SwiGLU pairs meet in one lane.  Four waves each own 128 rows
-// x 128 tokens (4 x 4 MFMA tiles, 256 fp32 accumulators per lane).  Thread t
-// decodes row t of the weight tile (its b plane words, the same byte
-// transpose and LUT-in-LDS lookups as the GEMV path) and stages token t of
-// the activation tile.  Weight and activation loads run two steps ahead in
-// a register ring; the two LDS stages alternate, one barrier per step.
+// rows, so the SwiGLU pairs meet in one lane.  Eight waves (two per SIMD)
+// each own 128 rows x 64 tokens (4 x 2 MFMA tiles, 128 fp32 accumulators per
+// lane).  Thread t < 256 (waves 0-3) decodes row t of the weight tile (its b
+// plane words, the same byte transpose and LUT-in-LDS lookups as the GEMV
+// path); thread 256 + t (waves 4-7) stages token t of the activation tile, so
+// each SIMD runs one decoding and one staging wave and the hardware overlaps
+// one wave's decode with the other's MFMAs.  Loads run three steps ahead in a
+// register ring; three LDS stages rotate, one barrier per step.
 // Items are (expert, row tile, token tile) with the token tile fastest, so
 // the workgroups the dispatcher sends to one XCD share that XCD's L2 copy of
 // a token tile while all XCDs walk the same weight rows.
@@ -32,7 +35,7 @@ namespace apmoe {
 
 namespace {
 
-constexpr int kThreadsTile = 256;
+constexpr int kThreadsTile = 512;
 constexpr int kTRows = 256;              // weight rows per tile (gate/up: 128 + 128)
 constexpr int kTToks = 256;              // tokens per tile
 constexpr int kRowB = 80;                // LDS bytes per tile row: 32 halves + 16 pad
@@ -100,18 +103,20 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
     const int r0 = it.rt * kMatRows, t0 = it.tt * kTToks;
+    const bool dec = wave < 4;   // role: decode weight row (waves 0-3) or stage token (4-7)
+    const int tr = tid & 255;    // the role's tile row / token
 
-    // decode role: tile row tid = matrix hsel, row r0 + (tid % kMatRows)
-    const int hsel = NMAT == 2 ? wave >> 1 : 0;   // gate/up: matrix (waves 2, 3: up); down: 0
-    const int rowc = min(r0 + tid % kMatRows, rows - 1);
+    // decode role: tile row tr = matrix hsel, row r0 + (tr % kMatRows)
+    const int hsel = NMAT == 2 ? (wave >> 1) & 1 : 0;   // gate/up: matrix (waves 2, 3: up); down: 0
+    const int rowc = min(r0 + tr % kMatRows, rows - 1);
     const apmoe_mat& mt = NMAT == 2 ? (hsel ? a.experts[it.e].up : a.experts[it.e].gate) : a.experts[it.e].down;
     const MatView mv = mat_view(mt, it.b);
     const uint32_t pbytes = 6u * (uint32_t)rows * 16u * (uint32_t)nsteps128;
     const uint32_t slab = (uint32_t)rows * 16u * (uint32_t)nsteps128;
     const uint32_t wbytes = (uint32_t)rows * (uint32_t)K * 2u;
 
-    // activation role: token t0 + tid of the group
-    const int tok = t0 + tid;
+    // activation role: token t0 + tr of the group
+    const int tok = t0 + tr;
     const bool tok_ok = tok < it.m;
     const int tokc = it.off + min(tok, it.m - 1);
     const int xrow = NMAT == 2 ? a.sorted_slots[tokc] / a.k : tokc;
@@ -144,22 +149,33 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
     const uint32_t lane_off = ((uint32_t)(wave & 1) << 16) |
                               (4u * (uint32_t)lane + 2u * (uint32_t)(NMAT == 2 ? hsel : (wave >> 1)));
 
-    constexpr int WR = B == 16 ? 4 : B;   // registers of one step's weights
-    uint32_t wreg[3][WR > 0 ? WR * (B == 16 ? 4 : 1) : 1];
-    half8_t xreg[3][4];
-    auto load = [&](int r, int s) {   // steps past ns read zeros
+    // one register ring for both roles: a step's 32 activations or its fp16
+    // weights (16 dwords), or its b plane words.  The role is a compile-time
+    // argument: each role runs its own copy of the step loop, so no branch
+    // splits a step and its MFMAs and decode share one scheduling region.
+    using DecRole = std::integral_constant<bool, true>;
+    using XRole = std::integral_constant<bool, false>;
+    uint32_t reg[3][16];
+    auto load = [&](auto role, int r, int s) {   // steps past ns read zeros
+        constexpr bool kDec = decltype(role)::value;
         const bool ok = s < ns;
-        const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.in, ok ? xbytes : 0u);
+        if constexpr (!kDec) {
+            const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.in, ok ? xbytes : 0u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xreg[r][j] = buf_load_h8(xr, tok_ok ? xbase + 64u * s + 16u * j : kOutOfRange);
-        if constexpr (B == 16) {
+            for (int j = 0; j < 4; ++j) {
+                const uint32x4_t v = __builtin_bit_cast(
+                    uint32x4_t, buf_load_h8(xr, tok_ok ? xbase + 64u * s + 16u * j : kOutOfRange));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) reg[r][4 * j + c] = v[c];
+            }
+        } else if constexpr (B == 16) {
             const __amdgpu_buffer_rsrc_t wr = make_rsrc((const void*)mv.w16, ok ? wbytes : 0u);
             const uint32_t base = ((uint32_t)rowc * (uint32_t)K + 32u * s) * 2u;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32x4_t v = __builtin_bit_cast(uint32x4_t, buf_load_h8(wr, base + 16u * j));
 #pragma unroll
-                for (int c = 0; c < 4; ++c) wreg[r][4 * j + c] = v[c];
+                for (int c = 0; c < 4; ++c) reg[r][4 * j + c] = v[c];
             }
         } else {
             const __amdgpu_buffer_rsrc_t pr = make_rsrc((const void*)mv.planes, ok ? pbytes : 0u);
@@ -167,24 +183,33 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
             const uint32_t at = ((uint32_t)(rowc >> 4) * (uint32_t)nsteps128 + (uint32_t)(sc >> 2)) * 256u +
                                 64u * (uint32_t)(sc & 3) + 4u * (uint32_t)(rowc & 15);
 #pragma unroll
-            for (int p = 0; p < B; ++p) wreg[r][p] = buf_load_u32(pr, at, p * slab);
+            for (int p = 0; p < B; ++p) reg[r][p] = buf_load_u32(pr, at, p * slab);
         }
     };
-    auto store = [&](int r, int st) {   // decode into LDS stage st
-        char* wt = lds + kStageOff[st] + tid * kRowB;
-        char* xt = lds + kStageOff[st] + kTileB + tid * kRowB;
-        if constexpr (B == 16) {
+    auto store = [&](auto role, int r, int st) {   // decode / stage into LDS stage st
+        constexpr bool kDec = decltype(role)::value;
+        char* wt = lds + kStageOff[st] + tr * kRowB;
+        if constexpr (!kDec) {
+            char* xt = wt + kTileB;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32x4_t v;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) v[c] = wreg[r][4 * j + c];
+                for (int c = 0; c < 4; ++c) v[c] = reg[r][4 * j + c];
+                *reinterpret_cast<uint32x4_t*>(xt + 16 * j) = v;
+            }
+        } else if constexpr (B == 16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32x4_t v;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[c] = reg[r][4 * j + c];
                 *reinterpret_cast<uint32x4_t*>(wt + 16 * j) = v;
             }
         } else {
             uint32_t q[8];
 #pragma unroll
-            for (int rr = 0; rr < 8; ++rr) q[rr] = rr < B ? wreg[r][B - 1 - rr] : 0u;   // bit rr <- plane B-1-rr
+            for (int rr = 0; rr < 8; ++rr) q[rr] = rr < B ? reg[r][B - 1 - rr] : 0u;   // bit rr <- plane B-1-rr
             transpose_bytes<B>(q);
             // byte u of q[j] is the code of column 8u + j.  All 32 lookups go
             // out before any store: a store between them would be ordered
@@ -203,22 +228,20 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
 #pragma unroll
             for (int u = 0; u < 4; ++u) *reinterpret_cast<uint32x4_t*>(wt + 16 * u) = v[u];
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<half8_t*>(xt + 16 * j) = xreg[r][j];
     };
 
-    // MFMA role: wave (wr, wt) owns tile rows {64wr + 32j, 128 + 64wr + 32j}
-    // (gate/up) or 128wr + 32j (down), j < 2 / 4, and tokens 128wt + 32i
+    // MFMA role: wave (wr, wtk) owns tile rows {64wr + 32j, 128 + 64wr + 32j}
+    // (gate/up) or 128wr + 32j (down), j < 2 / 4, and tokens 64wtk + 32i, i < 2
     const int wr = wave & 1, wtk = wave >> 1;
     int rbase[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         rbase[j] = NMAT == 2 ? (j < 2 ? 64 * wr + 32 * j : 128 + 64 * wr + 32 * (j - 2)) : 128 * wr + 32 * j;
-    float16_t acc[4][4];
+    float16_t acc[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
     const int l32 = lane & 31, lh = lane >> 5;
@@ -227,48 +250,54 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
         const char* xt = wt + kTileB;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            half8_t av[4], bv[4];
+            half8_t av[4], bv[2];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 av[j] = *reinterpret_cast<const half8_t*>(wt + (rbase[j] + l32) * kRowB + 32 * h + 16 * lh);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                bv[i] = *reinterpret_cast<const half8_t*>(xt + (128 * wtk + 32 * i + l32) * kRowB + 32 * h + 16 * lh);
+            for (int i = 0; i < 2; ++i)
+                bv[i] = *reinterpret_cast<const half8_t*>(xt + (64 * wtk + 32 * i + l32) * kRowB + 32 * h + 16 * lh);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 2; ++i)
                     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[i], acc[j][i], 0, 0, 0);
         }
     };
 
-    __syncthreads();   // LUT tables complete
-    load(0, 0);
-    load(1, 1);
-    load(2, 2);
-    store(0, 0);
-    __syncthreads();
     // Step st: refill the register slot step st left with step st + 3,
-    // multiply step st, decode step st + 1 (loaded two steps ago) into its
-    // stage.  No branch, so decode and MFMAs share one scheduling region, and
-    // the operand reads precede the stage writes in program order, so no
-    // assumed LDS alias holds the MFMAs behind the decode; steps past ns (at
-    // most two in the last group) read zeros and add nothing.
-    for (int s = 0; s < ns; s += 3) {
+    // multiply step st, decode / stage step st + 1 (loaded two steps ago)
+    // into its stage.  No branch inside a step, and the operand reads precede
+    // the stage writes in program order, so no assumed LDS alias holds the
+    // MFMAs behind the decode; steps past ns (at most two in the last group)
+    // read zeros and add nothing.  Both roles meet at the same barriers.
+    auto run = [&](auto role) {
+        load(role, 0, 0);
+        load(role, 1, 1);
+        load(role, 2, 2);
+        store(role, 0, 0);
+        __syncthreads();
+        for (int s = 0; s < ns; s += 3) {
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int st = s + u;
-            load(u, st + 3);
-            compute(u);                        // its LDS reads come before the writes below
-            store((u + 1) % 3, (u + 1) % 3);
-            __syncthreads();
+            for (int u = 0; u < 3; ++u) {
+                const int st = s + u;
+                load(role, u, st + 3);
+                compute(u);
+                store(role, (u + 1) % 3, (u + 1) % 3);
+                __syncthreads();
+            }
         }
-    }
+    };
+    __syncthreads();   // LUT tables complete
+    if (dec)
+        run(DecRole{});
+    else
+        run(XRole{});
 
     // D lane layout: row 8 * (r / 4) + 4 * (lane / 32) + r % 4, token lane % 32
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tk = t0 + 128 * wtk + 32 * i + l32;
+    for (int i = 0; i < 2; ++i) {
+        const int tk = t0 + 64 * wtk + 32 * i + l32;
         if (tk >= it.m) continue;
         const size_t p = (size_t)(it.off + tk);
 #pragma unroll
@@ -294,7 +323,7 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
 }
 
 template <int NMAT>
-__global__ __launch_bounds__(kThreadsTile) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsTile) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void tile_kernel(GemmArgs a, int RT) {
     __shared__ __attribute__((aligned(16))) char lds[kTileLds];
     TileItem it;
