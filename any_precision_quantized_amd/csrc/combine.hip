@@ -87,7 +87,7 @@ extern "C" size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I) {
     if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0) return 0;
     const size_t gu = gemv_workspace_bytes(T, k, E, I, H, 2);
     const size_t dn = gemv_workspace_bytes(T, k, E, H, I, 1);
-    const size_t rt = route_workspace_bytes(T, E);
+    const size_t rt = route_workspace_bytes(T, E, H);
     const size_t m = gu > dn ? gu : dn;
     return m > rt ? m : rt;
 }

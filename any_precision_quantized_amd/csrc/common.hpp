@@ -102,7 +102,7 @@ struct GemmArgs {
 };
 
 int launch_gemv(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
-size_t route_workspace_bytes(int T, int E);
+size_t route_workspace_bytes(int T, int E, int H);
 size_t gemv_workspace_bytes(int T, int k, int E, int rows, int K, int nmat);
 int launch_tile(const GemmArgs& a, hipStream_t s);
 

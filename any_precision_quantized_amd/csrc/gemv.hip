@@ -520,27 +520,11 @@ void gemv_kernel(GemmArgs a, int KS, float* partial) {
     }
 }
 
-// Sum the K-split partials in split order (SwiGLU for gate/up).  One thread
-// per (position, 4 rows); positions of tile-path groups are left alone.
+// Rows row..row+3 of position p: the K-split partial sums added in split
+// order, then SwiGLU (gate/up) or stored as they are (down).
 template <int NMAT>
-__global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, const float* partial) {
-    __shared__ int offs[APMOE_MAX_EXPERTS + 1];
-    for (int e = threadIdx.x; e <= a.E; e += blockDim.x) offs[e] = a.offsets[e];
-    __syncthreads();
-    const int rows = NMAT == 2 ? a.I : a.H;
-    const int S = a.T * a.k;
-    const int q4 = rows / 4;
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long long)S * q4) return;
-    const int p = (int)(idx / q4);
-    const int row = (int)(idx % q4) * 4;
-    int lo = 0, hi = a.E - 1;   // expert holding position p: last e with offs[e] <= p
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offs[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    const int m = offs[lo + 1] - offs[lo];
-    if (m >= a.mfma_min_tokens || !valid_bits(a.bits[lo])) return;
+__device__ __forceinline__ void finalize_rows(const GemmArgs& a, int KS, const float* partial, int S, int rows, int p,
+                                              int row) {
     float4_t s[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat) {
@@ -557,6 +541,32 @@ __global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, 
         *reinterpret_cast<half4_t*>(reinterpret_cast<half_t*>(a.out) + o) = h;
     } else {
         *reinterpret_cast<float4_t*>(reinterpret_cast<float*>(a.out) + o) = s[0];
+    }
+}
+
+// Sum the K-split partials in split order (SwiGLU for gate/up).  A workgroup
+// takes kFinPos consecutive positions; each wave finds a position's expert
+// and leaves positions of tile-path groups alone, so a launch over groups that
+// all took the tile path costs a few hundred short workgroups.
+constexpr int kFinPos = 64;
+template <int NMAT>
+__global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, const float* partial) {
+    __shared__ int offs[APMOE_MAX_EXPERTS + 1];
+    for (int e = threadIdx.x; e <= a.E; e += blockDim.x) offs[e] = a.offsets[e];
+    __syncthreads();
+    const int rows = NMAT == 2 ? a.I : a.H;
+    const int S = a.T * a.k;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int pend = min(S, (blockIdx.x + 1) * kFinPos);
+    for (int p = blockIdx.x * kFinPos + wave; p < pend; p += blockDim.x / kWave) {
+        int lo = 0, hi = a.E - 1;   // expert holding position p: last e with offs[e] <= p
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (offs[mid] <= p) lo = mid; else hi = mid - 1;
+        }
+        const int m = offs[lo + 1] - offs[lo];
+        if (m >= a.mfma_min_tokens || !valid_bits(a.bits[lo])) continue;   // uniform over the wave
+        for (int row = 4 * lane; row < rows; row += 4 * kWave) finalize_rows<NMAT>(a, KS, partial, S, rows, p, row);
     }
 }
 
@@ -606,8 +616,8 @@ int launch_gemv(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
         hipLaunchKernelGGL(gemv_kernel<1>, grid, block, 0, s, a, KS, partial);
     int rc = launch_status();
     if (rc != APMOE_OK || KS == 1) return rc;
-    const long long n = (long long)a.T * a.k * (rows / 4);
-    dim3 fgrid((unsigned)((n + 255) / 256));
+    const long long S = (long long)a.T * a.k;
+    dim3 fgrid((unsigned)((S + kFinPos - 1) / kFinPos));
     if (gu)
         hipLaunchKernelGGL(gemv_finalize_kernel<2>, fgrid, dim3(256), 0, s, a, KS, partial);
     else

@@ -1,6 +1,11 @@
 // Router: top-k over the router logits, then a softmax over the k chosen.
 //
-// Two kernels.  The logits kernel tiles (4 tokens x 8 experts) per workgroup:
+// Small problems run one kernel (route_kernel): a workgroup takes TB tokens
+// (more when T is large, so a router row read from L2 serves several tokens),
+// computes their logits for every expert into LDS and selects from there, so
+// no logit leaves the CU and the layer pays one launch.  Larger problems
+// (where one workgroup would stream too much of the router matrix) run two
+// kernels.  The logits kernel tiles (4 tokens x 8 experts) per workgroup:
 // wave w owns experts 2w, 2w+1 of the tile and its lanes split the hidden
 // dimension (four columns each per 256), so one 16-byte router-weight load
 // feeds four tokens and the tile's weights and activations cross the CU once.
@@ -67,23 +72,12 @@ __global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* _
         }
 }
 
-constexpr int kSelWaves = 4;
-
-__global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double* __restrict__ L, int T, int E, int k,
-                                                                    int32_t* __restrict__ topk_ids,
-                                                                    float* __restrict__ topk_w) {
-    __shared__ double chosen[kSelWaves][APMOE_MAX_EXPERTS];
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * kSelWaves + wave;
-    if (t >= T) return;   // uniform over the wave; no block barrier follows
-    constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
-    double v[kPer];
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-        const int e = lane + kWave * c;
-        v[c] = e < E ? L[(size_t)t * E + e] : -__builtin_inf();
-    }
+// k rounds of a wave-wide argmax over v (lane's experts lane + 64c), ties to
+// the lower expert, then the softmax over the chosen logits in fp64; lane 0
+// writes the results of token t.  chosen: k doubles of LDS for this wave.
+template <int kPer>
+__device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int t, int lane, double* chosen,
+                                            int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
     for (int j = 0; j < k; ++j) {
         double best = -__builtin_inf();
         int best_e = E;
@@ -103,21 +97,122 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
         for (int c = 0; c < kPer; ++c)
             if (lane + kWave * c == best_e) v[c] = -__builtin_inf();
         if (lane == 0) {
-            chosen[wave][j] = best;
+            chosen[j] = best;
             topk_ids[(size_t)t * k + j] = best_e;
         }
     }
     if (lane == 0) {
-        const double lmax = chosen[wave][0];
+        const double lmax = chosen[0];
         double sum = 0.0;
-        for (int j = 0; j < k; ++j) sum += exp(chosen[wave][j] - lmax);
-        for (int j = 0; j < k; ++j) topk_w[(size_t)t * k + j] = (float)(exp(chosen[wave][j] - lmax) / sum);
+        for (int j = 0; j < k; ++j) sum += exp(chosen[j] - lmax);
+        for (int j = 0; j < k; ++j) topk_w[(size_t)t * k + j] = (float)(exp(chosen[j] - lmax) / sum);
     }
+}
+
+// Fused router: TB tokens per workgroup, all E logits in LDS, then select.
+// Wave w takes experts in chunks of EC (chunk w, w + 4, ...); its lanes split
+// the hidden dimension as in the logits kernel.
+template <int TB>
+__global__ __launch_bounds__(kRWaves * kWave) void route_kernel(const half_t* __restrict__ x, int T, int H,
+                                                                 const float* __restrict__ w_router,
+                                                                 const float* __restrict__ bias, float scale, int E,
+                                                                 int k, int32_t* __restrict__ topk_ids,
+                                                                 float* __restrict__ topk_w) {
+    constexpr int EC = TB >= 16 ? 2 : (TB >= 8 ? 4 : 8);   // TB * EC <= 64 fp64 accumulators
+    __shared__ double L[TB][APMOE_MAX_EXPERTS];
+    __shared__ double chosen[kRWaves][APMOE_MAX_EXPERTS];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int t0 = blockIdx.x * TB;
+    const half_t* xr[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) xr[t] = x + (size_t)min(t0 + t, T - 1) * H;   // rows past T: a valid row, never used
+    for (int e0 = wave * EC; e0 < E; e0 += kRWaves * EC) {
+        const float* wr[EC];
+#pragma unroll
+        for (int j = 0; j < EC; ++j) wr[j] = w_router + (size_t)min(e0 + j, E - 1) * H;
+        double acc[TB][EC];
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int j = 0; j < EC; ++j) acc[t][j] = 0.0;
+#pragma unroll 2
+        for (int h = 4 * lane; h < H; h += 4 * kWave) {   // H % 32 == 0: h + 3 < H
+            float4v_t wv[EC];
+#pragma unroll
+            for (int j = 0; j < EC; ++j) wv[j] = *reinterpret_cast<const float4v_t*>(wr[j] + h);
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const half4_t xv = *reinterpret_cast<const half4_t*>(xr[t] + h);
+#pragma unroll
+                for (int j = 0; j < EC; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[t][j] = fma((double)xv[c], (double)wv[j][c], acc[t][j]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int j = 0; j < EC; ++j) {
+                const double sm = wave_sum(acc[t][j]);
+                const int e = e0 + j;
+                if (lane == 0 && e < E) L[t][e] = (double)scale * (sm + (bias ? (double)bias[e] : 0.0));
+            }
+    }
+    __syncthreads();
+    constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
+    for (int t = wave; t < TB; t += kRWaves) {
+        if (t0 + t >= T) break;   // uniform over the wave; no barrier follows
+        double v[kPer];
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) {
+            const int e = lane + kWave * c;
+            v[c] = e < E ? L[t][e] : -__builtin_inf();
+        }
+        select_topk<kPer>(v, E, k, t0 + t, lane, chosen[wave], topk_ids, topk_w);
+    }
+}
+
+constexpr int kSelWaves = 4;
+
+__global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double* __restrict__ L, int T, int E, int k,
+                                                                    int32_t* __restrict__ topk_ids,
+                                                                    float* __restrict__ topk_w) {
+    __shared__ double chosen[kSelWaves][APMOE_MAX_EXPERTS];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * kSelWaves + wave;
+    if (t >= T) return;   // uniform over the wave; no block barrier follows
+    constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
+    double v[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int e = lane + kWave * c;
+        v[c] = e < E ? L[(size_t)t * E + e] : -__builtin_inf();
+    }
+    select_topk<kPer>(v, E, k, t, lane, chosen[wave], topk_ids, topk_w);
 }
 
 }  // namespace
 
-size_t route_workspace_bytes(int T, int E) { return (size_t)(T > 0 ? T : 0) * (size_t)(E > 0 ? E : 0) * sizeof(double); }
+// Tokens per fused workgroup: the smallest power of two (at most 16) that
+// keeps the grid within 512 workgroups.  Every fused workgroup streams the
+// whole router matrix through its CU, so the fused kernel runs only when that
+// matrix is small (at most 160 KB, ~1 us at one CU's cache bandwidth) and one
+// workgroup's share stays small (at most 2^20 multiply-adds); otherwise the
+// two-kernel path, whose workgroups split the experts, runs.
+int fused_tokens(int T, int E, int H) {
+    int tb = 1;
+    while (tb < 16 && (T + tb - 1) / tb > 512) tb *= 2;
+    const double fmas = (double)tb * E * H;
+    const double wbytes = (double)E * H * 4.0;
+    return (fmas <= (double)(1 << 20) && wbytes <= 160.0 * 1024) ? tb : 0;
+}
+
+size_t route_workspace_bytes(int T, int E, int H) {
+    if (T <= 0 || E <= 0 || H <= 0 || fused_tokens(T, E, H)) return 0;
+    return (size_t)T * (size_t)E * sizeof(double);
+}
 
 }  // namespace apmoe
 
@@ -130,12 +225,27 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
     if (!(logit_scale > 0.0f)) return APMOE_EINVAL;
     if (T == 0) return APMOE_OK;
     if (!x || !w_router || !topk_ids || !topk_w) return APMOE_EINVAL;
-    if (!ws || ws_bytes < route_workspace_bytes(T, E)) return APMOE_ENOSPACE;
     hipStream_t s = as_stream(stream);
+    const half_t* xh = reinterpret_cast<const half_t*>(x);
+    switch (fused_tokens(T, E, H)) {
+#define APMOE_ROUTE_FUSED(TB_)                                                                                 \
+    case TB_:                                                                                                  \
+        hipLaunchKernelGGL(route_kernel<TB_>, dim3((T + TB_ - 1) / TB_), dim3(kRWaves * kWave), 0, s, xh, T, H, \
+                           w_router, bias, logit_scale, E, k, topk_ids, topk_w);                              \
+        return launch_status();
+        APMOE_ROUTE_FUSED(1)
+        APMOE_ROUTE_FUSED(2)
+        APMOE_ROUTE_FUSED(4)
+        APMOE_ROUTE_FUSED(8)
+        APMOE_ROUTE_FUSED(16)
+#undef APMOE_ROUTE_FUSED
+        default: break;
+    }
+    if (!ws || ws_bytes < route_workspace_bytes(T, E, H)) return APMOE_ENOSPACE;
     double* L = reinterpret_cast<double*>(ws);
     dim3 grid((T + kTB - 1) / kTB, (E + kEB - 1) / kEB);
-    hipLaunchKernelGGL(logits_kernel, grid, dim3(kRWaves * kWave), 0, s, reinterpret_cast<const half_t*>(x), T, H,
-                       w_router, bias, logit_scale, E, L);
+    hipLaunchKernelGGL(logits_kernel, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale, E,
+                       L);
     int rc = launch_status();
     if (rc != APMOE_OK) return rc;
     hipLaunchKernelGGL(select_kernel, dim3((T + kSelWaves - 1) / kSelWaves), dim3(kSelWaves * kWave), 0, s, L, T, E,

@@ -91,7 +91,10 @@ typedef struct apmoe_expert {
  *  bias     fp32 [E] or NULL     logit_scale > 0
  *  topk_ids int32 [T][k] (out)   topk_w   fp32 [T][k] (out)
  *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I)
- *           bytes (the fp64 logits, T * E * 8 bytes); APMOE_ENOSPACE if short.
+ *           bytes.  Small problems (a token group's share of T * E * H
+ *           multiply-adds fits one workgroup) keep the logits on chip and
+ *           need none; larger ones stage the fp64 logits there (T * E * 8
+ *           bytes) and return APMOE_ENOSPACE if it is short.
  * Needs 1 <= k <= E <= APMOE_MAX_EXPERTS, H > 0 and H % 32 == 0.
  */
 int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const float* bias,

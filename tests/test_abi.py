@@ -44,10 +44,12 @@ def test_validation_before_launch():
     assert lib.apmoe_route(None, 4, 64, fake, None, 1.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL
     assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 300, 2, fake, fake, fake, big, None) == _lib.EINVAL
     assert lib.apmoe_route(fake, 4, 48, fake, None, 1.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL   # H % 32
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 2, fake, fake, fake, 4 * 8 * 8 - 1, None) == _lib.ENOSPACE
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 2, fake, fake, None, big, None) == _lib.ENOSPACE
+    # a problem too large for the one-kernel router stages logits in the workspace
+    assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, fake,
+                           4096 * 256 * 8 - 1, None) == _lib.ENOSPACE
+    assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, None, big, None) == _lib.ENOSPACE
     assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None, 0, None) == _lib.OK   # T = 0
-    assert _lib.workspace_bytes(4, 2, 8, 64, 64) >= 4 * 8 * 8
+    assert _lib.workspace_bytes(4096, 2, 256, 4096, 64) >= 4096 * 256 * 8   # staged router logits
     # permute
     assert lib.apmoe_permute(fake, 4, 0, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
     assert lib.apmoe_permute(None, 4, 2, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
