@@ -41,11 +41,11 @@ constexpr int kTToks = 256;              // tokens per tile
 constexpr int kRowB = 80;                // LDS bytes per tile row: 32 halves + 16 pad
 constexpr int kTileB = 256 * kRowB;
 // LDS map: LUT block 0 at 0, stage 0 (W0 | X0) at 16K, LUT block 1 at 64K,
-// stages 1 and 2 at 80K and 120K (the lookup permute puts the LUT block into
-// address byte 2).  Three stages: step s uses stage s % 3, the same index as
-// its register slot, so the loop unrolls by three with no branch in its body.
-constexpr int kStageOff[3] = {16384, 81920, 81920 + 2 * kTileB};
-constexpr int kTileLds = 81920 + 4 * kTileB;
+// stage 1 at 80K (the lookup permute puts the LUT block into address byte 2).
+// Two stages: step s uses stage s % 2, the same index as its register slot,
+// so the loop unrolls by two with no branch in its body.
+constexpr int kStageOff[2] = {16384, 81920};
+constexpr int kTileLds = 81920 + 2 * kTileB;
 static_assert(16384 + 2 * kTileB <= 65536, "stage 0 overlaps LUT block 1");
 static_assert(kTileLds <= 160 * 1024, "tile LDS exceeds 160 KiB");
 
@@ -155,7 +155,7 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
     // splits a step and its MFMAs and decode share one scheduling region.
     using DecRole = std::integral_constant<bool, true>;
     using XRole = std::integral_constant<bool, false>;
-    uint32_t reg[3][16];
+    uint32_t reg[2][16];
     auto load = [&](auto role, int r, int s) {   // steps past ns read zeros
         constexpr bool kDec = decltype(role)::value;
         const bool ok = s < ns;
@@ -245,45 +245,48 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
     const int l32 = lane & 31, lh = lane >> 5;
+    // all twelve operand reads of the step go out before its first MFMA
     auto compute = [&](int st) {
         const char* wt = lds + kStageOff[st];
         const char* xt = wt + kTileB;
+        half8_t av[2][4], bv[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            half8_t av[4], bv[2];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                av[j] = *reinterpret_cast<const half8_t*>(wt + (rbase[j] + l32) * kRowB + 32 * h + 16 * lh);
+                av[h][j] = *reinterpret_cast<const half8_t*>(wt + (rbase[j] + l32) * kRowB + 32 * h + 16 * lh);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                bv[i] = *reinterpret_cast<const half8_t*>(xt + (64 * wtk + 32 * i + l32) * kRowB + 32 * h + 16 * lh);
+                bv[h][i] = *reinterpret_cast<const half8_t*>(xt + (64 * wtk + 32 * i + l32) * kRowB + 32 * h + 16 * lh);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[j], bv[i], acc[j][i], 0, 0, 0);
-        }
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[h][j], bv[h][i], acc[j][i], 0, 0, 0);
     };
 
-    // Step st: refill the register slot step st left with step st + 3,
-    // multiply step st, decode / stage step st + 1 (loaded two steps ago)
-    // into its stage.  No branch inside a step, and the operand reads precede
-    // the stage writes in program order, so no assumed LDS alias holds the
-    // MFMAs behind the decode; steps past ns (at most two in the last group)
-    // read zeros and add nothing.  Both roles meet at the same barriers.
+    // Step st: refill the register slot step st left with step st + 2,
+    // multiply step st, decode / stage step st + 1 (loaded a step earlier)
+    // into the other stage (read last at step st - 1, before the barrier).
+    // No branch inside a step, and the operand reads precede the stage writes
+    // in program order, so no assumed LDS alias holds the MFMAs behind the
+    // decode; a step past ns (at most one in the last pair) reads zeros and
+    // adds nothing.  Both roles meet at the same barriers.
     auto run = [&](auto role) {
         load(role, 0, 0);
         load(role, 1, 1);
-        load(role, 2, 2);
         store(role, 0, 0);
         __syncthreads();
-        for (int s = 0; s < ns; s += 3) {
+        for (int s = 0; s < ns; s += 2) {
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
+            for (int u = 0; u < 2; ++u) {
                 const int st = s + u;
-                load(role, u, st + 3);
+                load(role, u, st + 2);
                 compute(u);
-                store(role, (u + 1) % 3, (u + 1) % 3);
+                store(role, 1 - u, 1 - u);
                 __syncthreads();
             }
         }

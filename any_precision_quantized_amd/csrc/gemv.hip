@@ -58,6 +58,8 @@
 // leave CUs idle), each split writes fp32 partial sums to the workspace and a
 // finalize kernel adds them in split order (and applies SwiGLU), so results
 // never depend on scheduling.
+#include <algorithm>
+
 #include "common.hpp"
 #include "decode.hpp"
 
@@ -544,29 +546,30 @@ __device__ __forceinline__ void finalize_rows(const GemmArgs& a, int KS, const f
     }
 }
 
-// Sum the K-split partials in split order (SwiGLU for gate/up).  A workgroup
-// takes kFinPos consecutive positions; each wave finds a position's expert
-// and leaves positions of tile-path groups alone, so a launch over groups that
-// all took the tile path costs a few hundred short workgroups.
-constexpr int kFinPos = 64;
+// Sum the K-split partials in split order (SwiGLU for gate/up).  Workgroup
+// (x, y) takes positions [x * pb, (x + 1) * pb) and rows [1024 y, 1024 y +
+// 1024), four rows per thread; positions of tile-path groups are left alone,
+// so a launch whose groups all took the tile path costs about a thousand
+// short workgroups.  pb is chosen on the host to keep the grid near that.
+constexpr int kFinRows = 4 * 256;
 template <int NMAT>
-__global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, const float* partial) {
+__global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, const float* partial, int pb) {
     __shared__ int offs[APMOE_MAX_EXPERTS + 1];
     for (int e = threadIdx.x; e <= a.E; e += blockDim.x) offs[e] = a.offsets[e];
     __syncthreads();
     const int rows = NMAT == 2 ? a.I : a.H;
     const int S = a.T * a.k;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int pend = min(S, (blockIdx.x + 1) * kFinPos);
-    for (int p = blockIdx.x * kFinPos + wave; p < pend; p += blockDim.x / kWave) {
+    const int row = blockIdx.y * kFinRows + 4 * threadIdx.x;
+    const int pend = min(S, (blockIdx.x + 1) * pb);
+    for (int p = blockIdx.x * pb; p < pend; ++p) {
         int lo = 0, hi = a.E - 1;   // expert holding position p: last e with offs[e] <= p
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (offs[mid] <= p) lo = mid; else hi = mid - 1;
         }
         const int m = offs[lo + 1] - offs[lo];
-        if (m >= a.mfma_min_tokens || !valid_bits(a.bits[lo])) continue;   // uniform over the wave
-        for (int row = 4 * lane; row < rows; row += 4 * kWave) finalize_rows<NMAT>(a, KS, partial, S, rows, p, row);
+        if (m >= a.mfma_min_tokens || !valid_bits(a.bits[lo])) continue;   // uniform over the workgroup
+        if (row < rows) finalize_rows<NMAT>(a, KS, partial, S, rows, p, row);
     }
 }
 
@@ -617,11 +620,13 @@ int launch_gemv(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
     int rc = launch_status();
     if (rc != APMOE_OK || KS == 1) return rc;
     const long long S = (long long)a.T * a.k;
-    dim3 fgrid((unsigned)((S + kFinPos - 1) / kFinPos));
+    const long long chunks = (rows + kFinRows - 1) / kFinRows;
+    const long long pb = std::max<long long>(1, S * chunks / 1024);   // about a thousand workgroups
+    dim3 fgrid((unsigned)((S + pb - 1) / pb), (unsigned)chunks);
     if (gu)
-        hipLaunchKernelGGL(gemv_finalize_kernel<2>, fgrid, dim3(256), 0, s, a, KS, partial);
+        hipLaunchKernelGGL(gemv_finalize_kernel<2>, fgrid, dim3(256), 0, s, a, KS, partial, (int)pb);
     else
-        hipLaunchKernelGGL(gemv_finalize_kernel<1>, fgrid, dim3(256), 0, s, a, KS, partial);
+        hipLaunchKernelGGL(gemv_finalize_kernel<1>, fgrid, dim3(256), 0, s, a, KS, partial, (int)pb);
     return launch_status();
 }
 
