@@ -1,11 +1,9 @@
 // Router: top-k over the router logits, then a softmax over the k chosen.
 //
-// Small problems run one kernel (route_kernel): a workgroup takes TB tokens
-// (more when T is large, so a router row read from L2 serves several tokens),
-// computes their logits for every expert into LDS and selects from there, so
-// no logit leaves the CU and the layer pays one launch.  Larger problems
-// (where one workgroup would stream too much of the router matrix) run two
-// kernels.  The logits kernel tiles (4 tokens x 8 experts) per workgroup:
+// A few tokens over a small router matrix run one kernel (route_kernel): a
+// workgroup takes one or two tokens, computes their logits for every expert
+// into LDS and selects from there, so no logit leaves the CU and the layer
+// pays one launch.  Everything else runs two kernels.  The logits kernel tiles (4 tokens x 8 experts) per workgroup:
 // wave w owns experts 2w, 2w+1 of the tile and its lanes split the hidden
 // dimension (four columns each per 256), so one 16-byte router-weight load
 // feeds four tokens and the tile's weights and activations cross the CU once.
@@ -110,24 +108,31 @@ __device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int
 }
 
 // Fused router: TB tokens per workgroup, all E logits in LDS, then select.
-// Wave w takes experts in chunks of EC (chunk w, w + 4, ...); its lanes split
-// the hidden dimension as in the logits kernel.
+// Sixteen waves: wave w sums the hidden-dimension quarter w % 4 for the
+// expert group w / 4 (experts in chunks of EC, chunk g, g + 4, ...), its lanes
+// splitting the quarter as in the logits kernel; the four quarter sums of a
+// logit then meet in a fixed order.  Dynamic LDS: P[4][TB][E] quarter sums
+// (P[0] becomes the logits), then k chosen logits per wave.
+constexpr int kFWaves = 16;
 template <int TB>
-__global__ __launch_bounds__(kRWaves * kWave) void route_kernel(const half_t* __restrict__ x, int T, int H,
+__global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __restrict__ x, int T, int H,
                                                                  const float* __restrict__ w_router,
                                                                  const float* __restrict__ bias, float scale, int E,
                                                                  int k, int32_t* __restrict__ topk_ids,
                                                                  float* __restrict__ topk_w) {
-    constexpr int EC = TB >= 16 ? 2 : (TB >= 8 ? 4 : 8);   // TB * EC <= 64 fp64 accumulators
-    __shared__ double L[TB][APMOE_MAX_EXPERTS];
-    __shared__ double chosen[kRWaves][APMOE_MAX_EXPERTS];
+    constexpr int EC = 8;   // TB * EC <= 16 fp64 accumulators
+    extern __shared__ double dyn[];
+    double* P = dyn;                                      // [4][TB][E]
+    double* chosen = dyn + 4 * TB * E;                    // [kFWaves][k]
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
+    const int hq = wave & 3, eg = wave >> 2;
+    const int Hq = H / 4;                                 // H % 32 == 0: a multiple of 8
     const int t0 = blockIdx.x * TB;
     const half_t* xr[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) xr[t] = x + (size_t)min(t0 + t, T - 1) * H;   // rows past T: a valid row, never used
-    for (int e0 = wave * EC; e0 < E; e0 += kRWaves * EC) {
+    for (int e0 = eg * EC; e0 < E; e0 += 4 * EC) {
         const float* wr[EC];
 #pragma unroll
         for (int j = 0; j < EC; ++j) wr[j] = w_router + (size_t)min(e0 + j, E - 1) * H;
@@ -136,8 +141,7 @@ __global__ __launch_bounds__(kRWaves * kWave) void route_kernel(const half_t* __
         for (int t = 0; t < TB; ++t)
 #pragma unroll
             for (int j = 0; j < EC; ++j) acc[t][j] = 0.0;
-#pragma unroll 2
-        for (int h = 4 * lane; h < H; h += 4 * kWave) {   // H % 32 == 0: h + 3 < H
+        for (int h = hq * Hq + 4 * lane; h < (hq + 1) * Hq; h += 4 * kWave) {
             float4v_t wv[EC];
 #pragma unroll
             for (int j = 0; j < EC; ++j) wv[j] = *reinterpret_cast<const float4v_t*>(wr[j] + h);
@@ -156,20 +160,26 @@ __global__ __launch_bounds__(kRWaves * kWave) void route_kernel(const half_t* __
             for (int j = 0; j < EC; ++j) {
                 const double sm = wave_sum(acc[t][j]);
                 const int e = e0 + j;
-                if (lane == 0 && e < E) L[t][e] = (double)scale * (sm + (bias ? (double)bias[e] : 0.0));
+                if (lane == 0 && e < E) P[(hq * TB + t) * E + e] = sm;
             }
     }
     __syncthreads();
+    for (int i = threadIdx.x; i < TB * E; i += blockDim.x) {
+        const int e = i % E;
+        const double sm = (P[i] + P[TB * E + i]) + (P[2 * TB * E + i] + P[3 * TB * E + i]);
+        P[i] = (double)scale * (sm + (bias ? (double)bias[e] : 0.0));
+    }
+    __syncthreads();
     constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
-    for (int t = wave; t < TB; t += kRWaves) {
+    for (int t = wave; t < TB; t += kFWaves) {
         if (t0 + t >= T) break;   // uniform over the wave; no barrier follows
         double v[kPer];
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
             const int e = lane + kWave * c;
-            v[c] = e < E ? L[t][e] : -__builtin_inf();
+            v[c] = e < E ? P[t * E + e] : -__builtin_inf();
         }
-        select_topk<kPer>(v, E, k, t0 + t, lane, chosen[wave], topk_ids, topk_w);
+        select_topk<kPer>(v, E, k, t0 + t, lane, chosen + wave * k, topk_ids, topk_w);
     }
 }
 
@@ -195,18 +205,18 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
 
 }  // namespace
 
-// Tokens per fused workgroup: the smallest power of two (at most 16) that
-// keeps the grid within 512 workgroups.  Every fused workgroup streams the
-// whole router matrix through its CU, so the fused kernel runs only when that
-// matrix is small (at most 160 KB, ~1 us at one CU's cache bandwidth) and one
-// workgroup's share stays small (at most 2^20 multiply-adds); otherwise the
-// two-kernel path, whose workgroups split the experts, runs.
+// The fused kernel pays off for a few tokens and a small router matrix:
+// every fused workgroup streams the whole matrix through its CU, and each
+// (token, expert) sum costs four wave reductions, so with more tokens the
+// reductions dominate.  It runs for T <= 32 (one or two tokens per workgroup)
+// when the matrix is at most 160 KB; otherwise the two-kernel path, whose
+// workgroups split the experts, runs.
 int fused_tokens(int T, int E, int H) {
-    int tb = 1;
-    while (tb < 16 && (T + tb - 1) / tb > 512) tb *= 2;
-    const double fmas = (double)tb * E * H;
+    if (T > 32) return 0;
+    const int tb = T > 16 ? 2 : 1;
     const double wbytes = (double)E * H * 4.0;
-    return (fmas <= (double)(1 << 20) && wbytes <= 160.0 * 1024) ? tb : 0;
+    const double lds = (4.0 * tb * E + (double)kFWaves * E) * sizeof(double);
+    return (wbytes <= 160.0 * 1024 && lds <= 65536.0) ? tb : 0;
 }
 
 size_t route_workspace_bytes(int T, int E, int H) {
@@ -228,16 +238,14 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
     hipStream_t s = as_stream(stream);
     const half_t* xh = reinterpret_cast<const half_t*>(x);
     switch (fused_tokens(T, E, H)) {
-#define APMOE_ROUTE_FUSED(TB_)                                                                                 \
-    case TB_:                                                                                                  \
-        hipLaunchKernelGGL(route_kernel<TB_>, dim3((T + TB_ - 1) / TB_), dim3(kRWaves * kWave), 0, s, xh, T, H, \
-                           w_router, bias, logit_scale, E, k, topk_ids, topk_w);                              \
+#define APMOE_ROUTE_FUSED(TB_)                                                                                \
+    case TB_:                                                                                                 \
+        hipLaunchKernelGGL(route_kernel<TB_>, dim3((T + TB_ - 1) / TB_), dim3(kFWaves * kWave),                \
+                           (4 * TB_ * E + kFWaves * k) * sizeof(double), s, xh, T, H, w_router, bias, logit_scale, \
+                           E, k, topk_ids, topk_w);                                                           \
         return launch_status();
         APMOE_ROUTE_FUSED(1)
         APMOE_ROUTE_FUSED(2)
-        APMOE_ROUTE_FUSED(4)
-        APMOE_ROUTE_FUSED(8)
-        APMOE_ROUTE_FUSED(16)
 #undef APMOE_ROUTE_FUSED
         default: break;
     }
