@@ -19,6 +19,8 @@ design notes of this repository.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 F64 = np.float64
@@ -91,6 +93,35 @@ def route_margin(L: np.ndarray, k: int) -> np.ndarray:
     if k >= L.shape[1]:
         return np.full(L.shape[0], np.inf)
     return s[:, k - 1] - s[:, k]
+
+
+# ----------------------------------------------------------------------------
+# Routing statistics: the planner's online inputs
+# ----------------------------------------------------------------------------
+
+def route_stats(x, ids, gates, E):
+    """Per-expert routing mass and routing-weighted input norm, float64.
+
+    The page's planner ("内存的饥饿游戏…", zhichai.net, section "三层感知：离线 +
+    路由 + 提示词") weighs a live count of how much routing each expert gets
+    (to protect the busy ones) and a prompt-dependent correction taken from
+    routing-weighted input norms.  Read plainly:
+        mass[e]  = sum over slots (t, j) routed to e of gates[t, j]
+        wnorm[e] = sum over the same slots of gates[t, j] * ||x_t||_2
+    """
+    xs = np.asarray(x, dtype=F64)
+    ids = np.asarray(ids)
+    g = np.asarray(gates, dtype=F64)
+    T, k = ids.shape
+    norms = [math.sqrt(sum(float(v) * float(v) for v in xs[t])) for t in range(T)]
+    mass = np.zeros(E, dtype=F64)
+    wnorm = np.zeros(E, dtype=F64)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            mass[e] += g[t, j]
+            wnorm[e] += g[t, j] * norms[t]
+    return mass, wnorm
 
 
 # ----------------------------------------------------------------------------

@@ -262,6 +262,40 @@ def test_router_ties_go_to_lower_index():
     np.testing.assert_allclose(gates[:, 0], gates[:, 1])
 
 
+def test_route_stats_hand_example():
+    # three tokens, rows of four ones (norm 2), k = 2 over four experts:
+    # expert 0 gets 0.7 + 0.1, expert 1 0.3 + 0.5, expert 2 0.5 + 0.9, expert 3 nothing
+    x = np.ones((3, 4), dtype=np.float16)
+    ids = np.array([[0, 1], [1, 2], [0, 2]])
+    gates = np.array([[0.7, 0.3], [0.5, 0.5], [0.1, 0.9]])
+    mass, wnorm = moe.route_stats(x, ids, gates, 4)
+    np.testing.assert_allclose(mass, [0.8, 0.8, 1.4, 0.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(wnorm, [1.6, 1.6, 2.8, 0.0], rtol=0, atol=1e-15)
+
+
+def test_route_stats_invariants():
+    rng = np.random.default_rng(11)
+    T, H, E, k = 40, 64, 9, 3
+    x = rng.normal(size=(T, H)).astype(np.float16)
+    w = rng.normal(0, 0.05, size=(E, H)).astype(np.float32)
+    ids, gates, _ = moe.route(x, w, None, 1.0, k)
+    mass, wnorm = moe.route_stats(x, ids, gates, E)
+    # every token's gates sum to one, so the masses sum to T
+    assert abs(mass.sum() - T) < 1e-12
+    # the same sums written as one-hot matrix products
+    onehot = np.zeros((T, E))
+    for j in range(k):
+        onehot[np.arange(T), ids[:, j]] += gates[:, j]
+    norms = np.linalg.norm(x.astype(np.float64), axis=1)
+    np.testing.assert_allclose(mass, onehot.sum(axis=0), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(wnorm, onehot.T @ norms, rtol=1e-13, atol=1e-15)
+    # each expert's norm-weighted sum lies between its mass times the smallest
+    # and the largest input norm; unrouted experts have exactly zero
+    assert np.all(wnorm >= mass * norms.min() - 1e-12) and np.all(wnorm <= mass * norms.max() + 1e-12)
+    unused = np.setdiff1d(np.arange(E), ids.reshape(-1))
+    assert np.all(mass[unused] == 0) and np.all(wnorm[unused] == 0)
+
+
 def test_grouping_invariants():
     rng = np.random.default_rng(4)
     E, T, k = 9, 37, 3
