@@ -45,6 +45,7 @@ def _lib():
         sig = {
             "apmoe_route": [_vp, _c_int, _c_int, _vp, _vp, ctypes.c_float, _c_int, _c_int, _vp, _vp, _vp,
                             _c_size, _vp],
+            "apmoe_route_stats": [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp],
             "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp],
             "apmoe_bitplane_lut_gemm": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                         _c_int, _c_int, _c_int, _vp, _c_size, _vp],
@@ -127,6 +128,19 @@ def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, ws=None, stream=N
                             _ptr(topk_ids, torch.int32, T * k, "topk_ids"),
                             _ptr(topk_w, torch.float32, T * k, "topk_w"), wsp, wsb, _stream(stream))
     _check(rc, "apmoe_route")
+
+
+def route_stats(x, topk_ids, topk_w, E, mass, wnorm, ws, stream=None):
+    """Per-expert routing mass and routing-weighted input norm (fp32 [E] each)."""
+    torch = _torch()
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    rc = _lib().apmoe_route_stats(_ptr(x, torch.float16, T * H, "x"), T, H,
+                                  _ptr(topk_ids, torch.int32, T * k, "topk_ids"),
+                                  _ptr(topk_w, torch.float32, T * k, "topk_w"), k, E,
+                                  _ptr(mass, torch.float32, E, "mass"), _ptr(wnorm, torch.float32, E, "wnorm"),
+                                  _ptr(ws, torch.uint8, ws.numel(), "ws"), ws.numel(), _stream(stream))
+    _check(rc, "apmoe_route_stats")
 
 
 def permute(topk_ids, E, counts, offsets, sorted_slots, pos_of_slot, n_shared=0, stream=None):

@@ -203,6 +203,50 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
     select_topk<kPer>(v, E, k, t, lane, chosen[wave], topk_ids, topk_w);
 }
 
+// Routing statistics (the planner's online inputs).  norms_kernel: one wave
+// per token, ||x_t||_2 with the squares summed in fp32 and met in a fixed
+// butterfly.  stats_kernel: one wave per expert scans the T*k slots (lane l
+// takes slots l, l + 64, ...) adding its gates and gate * norm in fp32; the
+// lanes meet in a fixed butterfly, so the sums never depend on scheduling.
+__global__ __launch_bounds__(4 * kWave) void norms_kernel(const half_t* __restrict__ x, int T, int H,
+                                                          float* __restrict__ norms) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;   // uniform over the wave; no barrier follows
+    const half_t* xr = x + (size_t)t * H;
+    float acc = 0.f;
+    for (int h = 4 * lane; h < H; h += 4 * kWave) {   // H % 32 == 0: h + 3 < H
+        const half4_t v = *reinterpret_cast<const half4_t*>(xr + h);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc = fmaf((float)v[c], (float)v[c], acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) norms[t] = sqrtf(acc);
+}
+
+__global__ __launch_bounds__(4 * kWave) void stats_kernel(const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ w, int S, int k,
+                                                          const float* __restrict__ norms, int E,
+                                                          float* __restrict__ mass, float* __restrict__ wnorm) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int e = blockIdx.x * 4 + wave;
+    if (e >= E) return;   // uniform over the wave; no barrier follows
+    float m = 0.f, n = 0.f;
+    for (int s = lane; s < S; s += kWave) {
+        if (ids[s] == e) {
+            const float g = w[s];
+            m += g;
+            n = fmaf(g, norms[s / k], n);
+        }
+    }
+    m = wave_sum(m);
+    n = wave_sum(n);
+    if (lane == 0) {
+        mass[e] = m;
+        wnorm[e] = n;
+    }
+}
+
 }  // namespace
 
 // The fused kernel pays off for a few tokens and a small router matrix:
@@ -258,5 +302,26 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
     if (rc != APMOE_OK) return rc;
     hipLaunchKernelGGL(select_kernel, dim3((T + kSelWaves - 1) / kSelWaves), dim3(kSelWaves * kWave), 0, s, L, T, E,
                        k, topk_ids, topk_w);
+    return launch_status();
+}
+
+extern "C" int apmoe_route_stats(const uint16_t* x, int T, int H, const int32_t* topk_ids, const float* topk_w,
+                                 int k, int E, float* mass, float* wnorm, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    if (T < 0 || H <= 0 || H % 32 || E < 1 || E > APMOE_MAX_EXPERTS || k < 1 || k > E) return APMOE_EINVAL;
+    if (!mass || !wnorm) return APMOE_EINVAL;
+    if (T > 0 && (!x || !topk_ids || !topk_w)) return APMOE_EINVAL;
+    if ((long long)T * k > (1ll << 30)) return APMOE_EINVAL;
+    if (T > 0 && (!ws || ws_bytes < (size_t)T * sizeof(float))) return APMOE_ENOSPACE;
+    hipStream_t s = as_stream(stream);
+    float* norms = reinterpret_cast<float*>(ws);
+    if (T > 0) {
+        hipLaunchKernelGGL(norms_kernel, dim3((T + 3) / 4), dim3(4 * kWave), 0, s, reinterpret_cast<const half_t*>(x),
+                           T, H, norms);
+        const int rc = launch_status();
+        if (rc != APMOE_OK) return rc;
+    }
+    hipLaunchKernelGGL(stats_kernel, dim3((E + 3) / 4), dim3(4 * kWave), 0, s, topk_ids, topk_w, T * k, k, norms, E,
+                       mass, wnorm);
     return launch_status();
 }

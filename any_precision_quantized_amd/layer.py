@@ -171,6 +171,10 @@ class MoELayer:
         self.out = torch.empty((T, H), dtype=torch.float16, **dev)
         nws = _lib.workspace_bytes(T, kk, E2, H, I)
         self.ws = torch.empty(nws, dtype=torch.uint8, **dev) if nws else None
+        # routing statistics for the planner (per routed expert) and their token norms
+        self.mass = torch.empty(E, dtype=torch.float32, **dev)
+        self.wnorm = torch.empty(E, dtype=torch.float32, **dev)
+        self.ws_stats = torch.empty(max(4 * T, 4), dtype=torch.uint8, **dev)
         if shared is not None and not n:
             # the shared expert runs on a side stream (default priority) with
             # its own workspace, overlapping routing and the routed experts
@@ -195,6 +199,26 @@ class MoELayer:
     def commit(self, bits):
         """Routed bitwidths (the always-on parts stay at 16)."""
         _lib.commit_bits(bits, self.bits[self.n_shared:])
+
+    def route_stats(self, x):
+        """Routing mass and routing-weighted input norm of every routed expert
+        over the last forward's routing (x: the input it routed), fp32 [E]
+        device tensors (reused by later calls)."""
+        _lib.route_stats(x, self.topk_ids, self.topk_w, self.E, self.mass, self.wnorm, self.ws_stats)
+        return self.mass, self.wnorm
+
+    def replan(self, x, levels, harm, nbytes, floor_bits, budget):
+        """Re-plan the routed experts' bitwidths from the offline harm table
+        scaled by this step's routing statistics (see harm_multipliers), commit
+        the plan in stream order and return (status, bits).  Synchronises to
+        read the statistics back."""
+        mass, wnorm = self.route_stats(x)
+        h = harm_multipliers(mass.cpu().numpy(), wnorm.cpu().numpy())[0]
+        status, bits = _lib.plan_bitwidths(levels, np.asarray(harm, dtype=np.float64) * h[:, None], nbytes,
+                                           floor_bits, budget)
+        if status == _lib.OK:
+            self.commit(bits)
+        return status, bits
 
     def forward(self, x, experts: Optional[ExpertTable] = None, shared: Optional[ExpertTable] = None):
         """x: device fp16 [T, H].  Returns the fp16 output [T, H] (a buffer reused by later calls)."""
@@ -230,6 +254,33 @@ class MoELayer:
             torch.cuda.current_stream().wait_event(self.ev_join)
         _lib.combine(self.Y, self.pos_of_slot, self.topk_w, T, k, H, ysh, self.out, n)
         return self.out
+
+
+def harm_multipliers(mass, wnorm):
+    """Per-expert multipliers of the offline harm table from one step's routing
+    statistics (host, float64).  The planner page ("内存的饥饿游戏…", zhichai.net,
+    section "三层感知：离线 + 路由 + 提示词") protects experts that receive more
+    routing and corrects the offline table with a residual taken from
+    routing-weighted input norms; it gives no formula.  Read plainly:
+        load[e]  = mass[e] / mean_e(mass)             (1 = an average share)
+        resid[e] = (wnorm[e] / mass[e]) / (sum wnorm / sum mass)
+                   (the mean input norm of e's tokens against the mean over all
+                   routed slots; 1 for an expert with no slots)
+        mult[e]  = load[e] * resid[e]
+    so an expert nobody routes to costs nothing to demote.  Returns
+    (mult, load, resid)."""
+    mass = np.asarray(mass, dtype=np.float64)
+    wnorm = np.asarray(wnorm, dtype=np.float64)
+    E = mass.size
+    tot_m, tot_n = float(mass.sum()), float(wnorm.sum())
+    if not (tot_m > 0 and tot_n > 0):
+        one = np.ones(E)
+        return one, one.copy(), one.copy()
+    load = mass / (tot_m / E)
+    routed = mass > 0
+    resid = np.ones(E)
+    resid[routed] = (wnorm[routed] / mass[routed]) / (tot_n / tot_m)
+    return load * resid, load, resid
 
 
 def from_inputs(inp, bits=None, mfma_min_tokens=DEFAULT_MFMA_MIN_TOKENS, device="cuda"):

@@ -102,6 +102,24 @@ int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const fl
                 size_t ws_bytes, void* stream);
 
 /*
+ * Routing statistics for the bitwidth planner, over the slots of one
+ * apmoe_route call ("内存的饥饿游戏：当 MoE 权重与 KV 缓存争夺 GPU 的每一字节",
+ * zhichai.net, section "三层感知：离线 + 路由 + 提示词": a live measure of how
+ * much routing each expert receives protects the busy experts, and a
+ * correction taken from routing-weighted input norms adjusts the offline
+ * sensitivity table for the current prompt).
+ *  mass[e]  = sum over slots (t, j) with topk_ids[t][j] == e of topk_w[t][j]
+ *  wnorm[e] = the same sum of topk_w[t][j] * ||x_t||_2
+ *  x fp16 [T][H]; topk_ids int32 [T][k] and topk_w fp32 [T][k] as apmoe_route
+ *  wrote them; mass, wnorm fp32 [E] (out), fp32 sums in a fixed order.
+ *  ws/ws_bytes  at least T * 4 bytes (the token norms); APMOE_ENOSPACE if short.
+ * Needs 1 <= k <= E <= APMOE_MAX_EXPERTS, H > 0 and H % 32 == 0; T = 0 gives
+ * zeros.
+ */
+int apmoe_route_stats(const uint16_t* x, int T, int H, const int32_t* topk_ids, const float* topk_w, int k,
+                      int E, float* mass, float* wnorm, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Group slots by expert (stable: within an expert, slots in ascending order).
  * Each token owns kk = k + n_shared slots.  n_shared >= 0 always-on experts
  * (a shared expert split into n_shared experts of the routed size, each taking

@@ -15,7 +15,7 @@ from oracle import planner as planner_ref
 def test_library_exports_header_symbols():
     lib = _lib._lib()
     names = _lib.header_symbols()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -50,6 +50,12 @@ def test_validation_before_launch():
     assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, None, big, None) == _lib.ENOSPACE
     assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None, 0, None) == _lib.OK   # T = 0
     assert _lib.workspace_bytes(4096, 2, 256, 4096, 64) >= 4096 * 256 * 8   # staged router logits
+    # route statistics
+    assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 9, 8, fake, fake, fake, big, None) == _lib.EINVAL   # k > E
+    assert lib.apmoe_route_stats(fake, 4, 48, fake, fake, 2, 8, fake, fake, fake, big, None) == _lib.EINVAL   # H % 32
+    assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 2, 8, None, fake, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 2, 8, fake, fake, fake, 15, None) == _lib.ENOSPACE
+    assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 2, 8, fake, fake, None, big, None) == _lib.ENOSPACE
     # permute
     assert lib.apmoe_permute(fake, 4, 0, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
     assert lib.apmoe_permute(None, 4, 2, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL

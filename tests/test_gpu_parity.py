@@ -138,6 +138,29 @@ def test_full_size_layer(name):
           f"groups {sorted(got['counts'].tolist(), reverse=True)[:8]}")
 
 
+@pytest.mark.parametrize("name", ["tiny", "qwen_decode", "mixtral_decode_t8", "e128_decode"])
+def test_route_stats(name):
+    """Per-expert routing mass and routing-weighted input norm (apmoe_route_stats)
+    against the oracle's statistics over its own routing."""
+    import torch
+    cfg = synth.get(name)
+    G.say(f"route stats {name}")
+    inp = G.inputs(cfg)
+    bits = resolve_bits(inp)
+    ids, gates, logits = moe.route(inp.x, inp.w_router, inp.bias, cfg.logit_scale, cfg.k)
+    mass_ref, wnorm_ref = moe.route_stats(inp.x, ids, gates, cfg.E)
+    layer, got = G.run_layer(inp, bits)
+    if G.check_route(inp, got, ids, gates, logits):
+        pytest.skip("a near-tie routed a token differently; its expert's sums legitimately differ")
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
+    mass, wnorm = layer.route_stats(x)
+    torch.cuda.synchronize()
+    # fp32 sums of at most T*k terms
+    np.testing.assert_allclose(mass.cpu().numpy(), mass_ref, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(wnorm.cpu().numpy(), wnorm_ref, rtol=1e-5, atol=1e-4)
+    assert abs(float(mass.sum()) - cfg.T) <= 1e-4 * cfg.T
+
+
 @pytest.mark.parametrize("rows,cols", [(16, 32), (32, 704), (48, 320), (64, 4096)])
 def test_pack_planes_layout(rows, cols):
     """Packed word [p][group][step][g][i] is canonical word 4*step + g of row

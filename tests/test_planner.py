@@ -102,3 +102,42 @@ def test_zipf_plan_keeps_hot_experts_high():
     hist = {b: int((bits == b).sum()) for b in (6, 5, 4, 3)}
     print("qwen plan histogram", hist, "mean bits", bits.mean())
     assert all(v > 0 for v in hist.values())
+
+
+# ---------------------------------------------------------------------------
+# Routing statistics -> planner multipliers (host logic of the layer)
+# ---------------------------------------------------------------------------
+
+def test_harm_multipliers_hand_values():
+    from any_precision_quantized_amd.layer import harm_multipliers
+    # equal input norms (2): the residual is 1 everywhere and the multiplier is
+    # the expert's share of routing against an even 3/4 per expert
+    mult, load, resid = harm_multipliers([0.8, 0.8, 1.4, 0.0], [1.6, 1.6, 2.8, 0.0])
+    np.testing.assert_allclose(load, [16 / 15, 16 / 15, 28 / 15, 0.0], rtol=1e-15)
+    np.testing.assert_allclose(resid, [1.0, 1.0, 1.0, 1.0], rtol=1e-15)
+    np.testing.assert_allclose(mult, load, rtol=1e-15)
+    # equal routing, inputs of norm 1 and 3: residuals 1/2 and 3/2 of the mean 2
+    mult, load, resid = harm_multipliers([1.0, 1.0], [1.0, 3.0])
+    np.testing.assert_allclose(load, [1.0, 1.0])
+    np.testing.assert_allclose(resid, [0.5, 1.5])
+    np.testing.assert_allclose(mult, [0.5, 1.5])
+    # nothing routed: the offline table stands
+    mult, _, _ = harm_multipliers([0.0, 0.0, 0.0], [0.0, 0.0, 0.0])
+    np.testing.assert_allclose(mult, [1.0, 1.0, 1.0])
+
+
+def test_harm_multipliers_demote_idle_experts_first():
+    from any_precision_quantized_amd import _lib
+    from any_precision_quantized_amd.layer import harm_multipliers
+    levels = np.array([6, 5, 4, 3], np.int8)
+    E = 4
+    harm = np.tile(np.array([0.0, 2.0 ** -5, 2.0 ** -4, 2.0 ** -3]), (E, 1))   # the same offline table
+    nbytes = np.tile(np.array([600, 500, 400, 300], np.uint64), (E, 1))
+    floors = np.full(E, 3, np.int8)
+    mult, _, _ = harm_multipliers([1.5, 0.0, 1.0, 1.5], [3.0, 0.0, 2.0, 3.0])
+    budget = 4 * 600 - 300          # room for one expert at 3 bits
+    st, bits = _lib.plan_bitwidths(levels, harm * mult[:, None], nbytes, floors, budget)
+    assert st == _lib.OK
+    assert bits.tolist() == [6, 3, 6, 6]   # the expert nobody routes to goes first, to its floor
+    st, ref = planner.plan_bitwidths(levels, harm * mult[:, None], nbytes, floors, budget)
+    assert st == planner.OK and ref.tolist() == bits.tolist()
