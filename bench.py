@@ -269,6 +269,18 @@ def main():
         torch.cuda.synchronize()
         per[name] = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3   # us
     dominant = max(names, key=lambda n: per[n])
+    # routing statistics for the planner (outside the layer step: the planner
+    # reads them at a step boundary), timed the same way
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(probe_steps)]
+    for i in range(probe_steps):
+        evs[i][0].record(stream)
+        rc = lib.apmoe_route_stats(p(x), T, H, p(layer.topk_ids), p(layer.topk_w), k, E, p(layer.mass),
+                                   p(layer.wnorm), p(layer.ws_stats), layer.ws_stats.numel(), sp)
+        evs[i][1].record(stream)
+        if rc != 0:
+            raise _lib.ApmoeError(rc, "route_stats")
+    torch.cuda.synchronize()
+    route_stats_us = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3
 
     # Timed region: K whole steps; the dominant launch is bracketed by events.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -323,6 +335,7 @@ def main():
         "expert_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "roofline": roofline,
         "per_launch_us": {n: round(per[n], 2) for n in names},
+        "route_stats_us": round(route_stats_us, 2),
         "per_launch_bytes": {n: int(by.get(n, 0)) for n in names},
     }
     if not args.no_cpu_baseline:

@@ -98,3 +98,49 @@ def brute_force(levels, harm, nbytes, floor_bits, budget):
     if best is None:
         return None, None
     return best[0], np.array([levels[l] for l in best[1]], dtype=np.int8)
+
+
+def online_step(levels, harm, nbytes, floor_bits, stage_bits, m_total, m_kv, hysteresis, bits_now):
+    """One step of the online planner under the KV budget.
+
+    The planner page searches several bitwidth stages, starting from the
+    safest demotion plan and moving to more aggressive ones only when pressure
+    demands it, never below an expert's floor ("内存的饥饿游戏", zhichai.net,
+    section "安全边界与异步搬运"); the second summary recomputes the weight
+    budget M_w = M_total - M_kv as the KV cache grows ("动态量化优化MoE模型服务",
+    time-frame.cloud, section "方法与技术路线").  Reading taken here:
+
+    * stage_bits[s] (high to low) is the lowest bitwidth stage s may use: an
+      expert's floor in stage s is the higher of its own floor and
+      stage_bits[s]; the stage's plan for a budget is the demotion-sequence
+      greedy under those floors;
+    * the current plan is kept while it fits M_w with less than `hysteresis`
+      bytes to spare; otherwise (over M_w, or hysteresis or more to spare) the
+      plan is recomputed for M_w - hysteresis: the first stage whose plan fits
+      that; if none does, the first stage whose plan fits M_w; if none does,
+      every expert at its last-stage floor with status ENOSPACE.
+
+    Returns (status, bits[E], stage, changed); stage is -1 when the plan is kept.
+    """
+    levels = [int(v) for v in levels]
+    E = len(floor_bits)
+    m_w = max(0, int(m_total) - int(m_kv))
+    now = [int(b) for b in bits_now]
+    used = plan_total(levels, nbytes, now)
+    h = int(hysteresis)
+    if used <= m_w and m_w - used < h:
+        return OK, np.array(now, dtype=np.int8), -1, False
+    target = max(0, m_w - h)
+
+    def stage_floors(s):
+        return np.array([max(int(floor_bits[e]), int(stage_bits[s])) for e in range(E)], dtype=np.int8)
+
+    for budget in (target, m_w):
+        for s in range(len(stage_bits)):
+            st, bits = plan_bitwidths(levels, harm, nbytes, stage_floors(s), budget)
+            if st == EINVAL:
+                return EINVAL, None, -1, False
+            if st == OK:
+                return OK, bits, s, bits.tolist() != now
+    last = stage_floors(len(stage_bits) - 1)
+    return ENOSPACE, last, len(stage_bits) - 1, last.tolist() != now

@@ -141,3 +141,87 @@ def test_harm_multipliers_demote_idle_experts_first():
     assert bits.tolist() == [6, 3, 6, 6]   # the expert nobody routes to goes first, to its floor
     st, ref = planner.plan_bitwidths(levels, harm * mult[:, None], nbytes, floors, budget)
     assert st == planner.OK and ref.tolist() == bits.tolist()
+
+
+# ---------------------------------------------------------------------------
+# Online planner under the KV budget (oracle pins)
+# ---------------------------------------------------------------------------
+
+def _online_case():
+    levels = [6, 5, 4, 3]
+    harm = np.array([[0.0, 1.0, 3.0, 7.0],       # expert 0: sensitive
+                     [0.0, 0.1, 0.3, 0.7],       # expert 1: tolerant
+                     [0.0, 0.5, 1.5, 3.5]])
+    nbytes = np.array([[600, 500, 400, 300]] * 3, dtype=np.uint64)
+    floors = np.array([4, 3, 3], np.int8)
+    stages = [5, 4, 3]
+    return levels, harm, nbytes, floors, stages
+
+
+def test_online_ample_budget_keeps_full_precision():
+    levels, harm, nbytes, floors, stages = _online_case()
+    st, bits, stage, changed = planner.online_step(levels, harm, nbytes, floors, stages, 10_000, 0, 100,
+                                                   [3, 3, 3])
+    assert st == planner.OK and bits.tolist() == [6, 6, 6] and stage == 0 and changed
+
+
+def test_online_stages_escalate_only_under_pressure():
+    levels, harm, nbytes, floors, stages = _online_case()
+    # 1500 of 1800 bytes: three 100-byte demotions; stage 0 (nobody below 5)
+    # allows exactly one per expert
+    st, bits, stage, _ = planner.online_step(levels, harm, nbytes, floors, stages, 1500, 0, 0, [6, 6, 6])
+    assert st == planner.OK and stage == 0 and bits.tolist() == [5, 5, 5]
+    # 1600 bytes: two demotions, the tolerant expert then the middle one
+    st, bits, stage, _ = planner.online_step(levels, harm, nbytes, floors, stages, 1600, 0, 0, [6, 6, 6])
+    assert st == planner.OK and stage == 0 and bits.tolist() == [6, 5, 5]
+    # 1300 bytes: stage 0 bottoms out at 1500, stage 1 (down to 4 bits) fits
+    st, bits, stage, _ = planner.online_step(levels, harm, nbytes, floors, stages, 1300, 0, 0, [5, 5, 5])
+    assert st == planner.OK and stage == 1
+    assert planner.plan_total(levels, nbytes, bits) <= 1300 and min(bits) >= 4
+    # 1000 bytes: only stage 2 fits; the sensitive expert keeps its own floor of 4
+    st, bits, stage, _ = planner.online_step(levels, harm, nbytes, floors, stages, 1000, 0, 0, [6, 6, 6])
+    assert st == planner.OK and stage == 2 and bits[0] >= 4
+    assert planner.plan_total(levels, nbytes, bits) <= 1000
+    # below every floor: floors of the last stage, ENOSPACE
+    st, bits, stage, _ = planner.online_step(levels, harm, nbytes, floors, stages, 900, 0, 0, [6, 6, 6])
+    assert st == planner.ENOSPACE and bits.tolist() == [4, 3, 3] and stage == 2
+
+
+def test_online_budget_is_total_minus_kv_and_hysteresis_band_keeps_the_plan():
+    levels, harm, nbytes, floors, stages = _online_case()
+    # M_w = 2000 - 400 = 1600 with hysteresis 100: replanned for 1500
+    st, bits, stage, changed = planner.online_step(levels, harm, nbytes, floors, stages, 2000, 400, 100,
+                                                   [6, 6, 6])
+    assert st == planner.OK and changed and planner.plan_total(levels, nbytes, bits) <= 1500
+    # KV grows by 50: the plan (1500 bytes) still fits 1550 with less than 100 spare -> kept
+    st2, bits2, stage2, changed2 = planner.online_step(levels, harm, nbytes, floors, stages, 2000, 450, 100, bits)
+    assert st2 == planner.OK and stage2 == -1 and not changed2 and bits2.tolist() == bits.tolist()
+    # KV shrinks back to 300: 200 spare >= 100 -> replanned for 1600, a promotion
+    st3, bits3, stage3, changed3 = planner.online_step(levels, harm, nbytes, floors, stages, 2000, 300, 100, bits)
+    assert st3 == planner.OK and changed3 and planner.plan_total(levels, nbytes, bits3) <= 1600
+    assert planner.plan_total(levels, nbytes, bits3) > planner.plan_total(levels, nbytes, bits)
+    assert all(int(a) >= int(b) for a, b in zip(bits3, bits))
+
+
+def test_online_first_feasible_stage_is_chosen():
+    rng = np.random.default_rng(5)
+    levels = [6, 5, 4, 3]
+    stages = [5, 4, 3]
+    for _ in range(50):
+        E = int(rng.integers(2, 6))
+        harm = np.cumsum(rng.uniform(0, 1, size=(E, 4)), axis=1) - rng.uniform(0, 1, size=(E, 1))
+        harm[:, 0] = 0.0
+        harm = np.maximum.accumulate(np.abs(harm), axis=1)
+        nbytes = np.array([[600, 500, 400, 300]] * E, dtype=np.uint64)
+        floors = rng.choice([3, 4], size=E).astype(np.int8)
+        budget = int(rng.integers(300 * E, 600 * E + 1))
+        st, bits, stage, _ = planner.online_step(levels, harm, nbytes, floors, stages, budget, 0, 0, [6] * E)
+        fits = []
+        for s, sb in enumerate(stages):
+            f = np.maximum(floors, sb).astype(np.int8)
+            fits.append(planner.plan_bitwidths(levels, harm, nbytes, f, budget)[0] == planner.OK)
+        if any(fits):
+            assert st == planner.OK and stage == fits.index(True)
+            assert planner.plan_total(levels, nbytes, bits) <= budget
+        else:
+            assert st == planner.ENOSPACE
