@@ -51,6 +51,8 @@ def _lib():
                                         _c_int, _c_int, _c_int, _vp, _c_size, _vp],
             "apmoe_combine": [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp],
             "apmoe_plan_bitwidths": [_c_int, _c_int, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp],
+            "apmoe_plan_online": [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, ctypes.c_uint64,
+                                  ctypes.c_uint64, ctypes.c_uint64, _vp, _vp, _vp],
             "apmoe_commit_bits": [_vp, _c_int, _vp, _vp],
             "apmoe_workspace_bytes": [_c_int, _c_int, _c_int, _c_int, _c_int],
             "apmoe_packed_plane_words": [_c_int, _c_int],
@@ -231,3 +233,26 @@ def plan_bitwidths(levels, harm, nbytes, floor_bits, budget):
     rc = _lib().apmoe_plan_bitwidths(E, L, lv.ctypes.data, hm.ctypes.data, nb.ctypes.data,
                                      fl.ctypes.data, int(budget), out.ctypes.data)
     return rc, out
+
+
+def plan_online(levels, harm, nbytes, floor_bits, stage_bits, m_total, m_kv, hysteresis, bits_now):
+    """Online planner step.  Returns (status, bits int8[E], stage); stage is -1
+    when the current plan is kept.  Raises only on EINVAL/EBITS."""
+    import numpy as np
+    lv = np.ascontiguousarray(np.asarray(levels, dtype=np.int8))
+    hm = np.ascontiguousarray(np.asarray(harm, dtype=np.float64))
+    nb = np.ascontiguousarray(np.asarray(nbytes, dtype=np.uint64))
+    fl = np.ascontiguousarray(np.asarray(floor_bits, dtype=np.int8))
+    sb = np.ascontiguousarray(np.asarray(stage_bits, dtype=np.int8))
+    now = np.ascontiguousarray(np.asarray(bits_now, dtype=np.int8))
+    E, L = hm.shape
+    if nb.shape != (E, L) or lv.shape != (L,) or fl.shape != (E,) or now.shape != (E,):
+        raise ValueError("planner input shapes disagree")
+    out = np.zeros(E, dtype=np.int8)
+    stage = ctypes.c_int(0)
+    rc = _lib().apmoe_plan_online(E, L, lv.ctypes.data, hm.ctypes.data, nb.ctypes.data, fl.ctypes.data, len(sb),
+                                  sb.ctypes.data, int(m_total), int(m_kv), int(hysteresis), now.ctypes.data,
+                                  out.ctypes.data, ctypes.byref(stage))
+    if rc not in (OK, ENOSPACE):
+        _check(rc, "apmoe_plan_online")
+    return rc, out, stage.value

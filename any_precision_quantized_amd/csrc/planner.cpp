@@ -76,3 +76,61 @@ extern "C" int apmoe_plan_bitwidths(int E, int L, const int8_t* levels, const do
     for (int e = 0; e < E; ++e) bits_out[e] = levels[lvl[e]];
     return APMOE_OK;
 }
+
+// One step of the online planner under the KV budget.  The weight budget is
+// M_w = M_total - M_kv ("动态量化优化MoE模型服务", time-frame.cloud, section
+// "方法与技术路线"); the search walks bitwidth stages from the safest to the most
+// aggressive and stops at the first that fits, never below an expert's floor
+// ("内存的饥饿游戏", zhichai.net, section "安全边界与异步搬运").  Stage s lets no
+// expert below stage_bits[s] (nor below its own floor).  The current plan is
+// kept while it fits M_w with less than `hysteresis` bytes to spare;
+// otherwise the plan is recomputed for M_w - hysteresis, then for M_w.
+extern "C" int apmoe_plan_online(int E, int L, const int8_t* levels, const double* harm, const uint64_t* bytes,
+                                 const int8_t* floor_bits, int n_stages, const int8_t* stage_bits,
+                                 uint64_t m_total, uint64_t m_kv, uint64_t hysteresis, const int8_t* bits_now,
+                                 int8_t* bits_out, int* stage_out) {
+    if (E < 1 || E > APMOE_MAX_EXPERTS || L < 1 || L > 5 || n_stages < 1 || n_stages > 5) return APMOE_EINVAL;
+    if (!levels || !harm || !bytes || !floor_bits || !stage_bits || !bits_now || !bits_out || !stage_out)
+        return APMOE_EINVAL;
+    auto level_of = [&](int b) {
+        for (int l = 0; l < L; ++l)
+            if (levels[l] == b) return l;
+        return -1;
+    };
+    for (int l = 0; l < L; ++l)
+        if (!valid_level(levels[l])) return APMOE_EBITS;
+    for (int s = 0; s < n_stages; ++s)
+        if (level_of(stage_bits[s]) < 0) return APMOE_EINVAL;
+    const uint64_t m_w = m_total > m_kv ? m_total - m_kv : 0;
+    uint64_t used = 0;
+    for (int e = 0; e < E; ++e) {
+        const int l = level_of(bits_now[e]);
+        if (l < 0) return APMOE_EINVAL;
+        used += bytes[(size_t)e * L + l];
+    }
+    if (used <= m_w && m_w - used < hysteresis) {
+        for (int e = 0; e < E; ++e) bits_out[e] = bits_now[e];
+        *stage_out = -1;
+        return APMOE_OK;
+    }
+    std::vector<int8_t> floors(E);
+    auto stage_floors = [&](int s) {
+        for (int e = 0; e < E; ++e) floors[e] = floor_bits[e] > stage_bits[s] ? floor_bits[e] : stage_bits[s];
+    };
+    const uint64_t target = m_w > hysteresis ? m_w - hysteresis : 0;
+    for (uint64_t budget : {target, m_w}) {
+        for (int s = 0; s < n_stages; ++s) {
+            stage_floors(s);
+            const int rc = apmoe_plan_bitwidths(E, L, levels, harm, bytes, floors.data(), budget, bits_out);
+            if (rc == APMOE_OK) {
+                *stage_out = s;
+                return APMOE_OK;
+            }
+            if (rc != APMOE_ENOSPACE) return rc;
+        }
+    }
+    stage_floors(n_stages - 1);
+    for (int e = 0; e < E; ++e) bits_out[e] = floors[e];
+    *stage_out = n_stages - 1;
+    return APMOE_ENOSPACE;
+}

@@ -283,6 +283,41 @@ def harm_multipliers(mass, wnorm):
     return load * resid, load, resid
 
 
+class OnlinePlanner:
+    """The layer's bitwidth plan kept up to date as the KV cache grows and
+    shrinks: each step recomputes the weight budget M_w = m_total - m_kv and
+    runs the staged, floored, hysteretic planner step (apmoe_plan_online); a
+    changed plan is committed to the layer in stream order, so the next
+    forward call uses it.  `harm` may be replaced per step (for example by the
+    offline table scaled with harm_multipliers of the last routing)."""
+
+    def __init__(self, layer, levels, harm, nbytes, floor_bits, stage_bits, m_total, hysteresis, bits_now):
+        self.layer = layer
+        self.levels = np.asarray(levels, dtype=np.int8)
+        self.harm = np.asarray(harm, dtype=np.float64)
+        self.nbytes = np.asarray(nbytes, dtype=np.uint64)
+        self.floor_bits = np.asarray(floor_bits, dtype=np.int8)
+        self.stage_bits = np.asarray(stage_bits, dtype=np.int8)
+        self.m_total = int(m_total)
+        self.hysteresis = int(hysteresis)
+        self.bits = np.asarray(bits_now, dtype=np.int8).copy()
+        self.stage = -1
+
+    def step(self, m_kv, harm=None):
+        """Returns (status, bits, stage, changed); stage -1 = plan kept."""
+        if harm is not None:
+            self.harm = np.asarray(harm, dtype=np.float64)
+        status, bits, stage = _lib.plan_online(self.levels, self.harm, self.nbytes, self.floor_bits,
+                                               self.stage_bits, self.m_total, m_kv, self.hysteresis, self.bits)
+        changed = bits.tolist() != self.bits.tolist()
+        if changed:
+            self.layer.commit(bits)
+            self.bits = bits
+        if stage >= 0:
+            self.stage = stage
+        return status, bits, stage, changed
+
+
 def from_inputs(inp, bits=None, mfma_min_tokens=DEFAULT_MFMA_MIN_TOKENS, device="cuda"):
     """Build device weights and a layer from a generated input set (duck-typed)."""
     cfg = inp.cfg

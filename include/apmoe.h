@@ -206,6 +206,30 @@ int apmoe_plan_bitwidths(int E, int L, const int8_t* levels, const double* harm,
  */
 int apmoe_commit_bits(const int8_t* bits_host, int E, int8_t* bits_dev, void* stream);
 
+/*
+ * One step of the online bitwidth planner as the KV cache grows or shrinks
+ * (host only).  The weight budget is M_w = max(0, m_total - m_kv)
+ * ("动态量化优化MoE模型服务", time-frame.cloud, section "方法与技术路线"); the
+ * search walks bitwidth stages from the safest to the most aggressive and
+ * stops at the first that fits, never below an expert's floor ("内存的饥饿游戏：
+ * 当 MoE 权重与 KV 缓存争夺 GPU 的每一字节", zhichai.net, section "安全边界与异步搬运").
+ *  levels, harm, bytes, floor_bits  as apmoe_plan_bitwidths (host arrays)
+ *  stage_bits [n_stages]  lowest bitwidth of each stage, safest first (each one
+ *                         of levels); in stage s an expert's floor is the
+ *                         higher of floor_bits[e] and stage_bits[s]
+ *  hysteresis             the current plan is kept while it fits M_w with less
+ *                         than this many bytes to spare; otherwise the plan is
+ *                         recomputed for M_w - hysteresis, then for M_w
+ *  bits_now [E]           the current plan;  bits_out [E] the new plan
+ *  stage_out              stage of the new plan, -1 when the current plan is kept
+ * Returns APMOE_OK, or APMOE_ENOSPACE with every expert at its last-stage
+ * floor when no stage fits; APMOE_EINVAL / APMOE_EBITS on bad input.
+ */
+int apmoe_plan_online(int E, int L, const int8_t* levels, const double* harm, const uint64_t* bytes,
+                      const int8_t* floor_bits, int n_stages, const int8_t* stage_bits, uint64_t m_total,
+                      uint64_t m_kv, uint64_t hysteresis, const int8_t* bits_now, int8_t* bits_out,
+                      int* stage_out);
+
 /* Workspace bytes apmoe_route and apmoe_bitplane_lut_gemm need for these
  * shapes (one buffer serves both; calls that share it must not overlap). */
 size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I);

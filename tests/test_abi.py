@@ -15,7 +15,7 @@ from oracle import planner as planner_ref
 def test_library_exports_header_symbols():
     lib = _lib._lib()
     names = _lib.header_symbols()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -56,6 +56,18 @@ def test_validation_before_launch():
     assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 2, 8, None, fake, fake, big, None) == _lib.EINVAL
     assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 2, 8, fake, fake, fake, 15, None) == _lib.ENOSPACE
     assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 2, 8, fake, fake, None, big, None) == _lib.ENOSPACE
+    # online planner: no stages, a stage bitwidth that is not a level
+    lv = np.array([6, 5, 4, 3], np.int8)
+    hm = np.zeros((2, 4))
+    nb = np.array([[600, 500, 400, 300]] * 2, dtype=np.uint64)
+    fl = np.array([3, 3], np.int8)
+    now = np.array([6, 6], np.int8)
+    out = np.zeros(2, np.int8)
+    stage = ctypes.c_int(0)
+    for sb, n in ((np.array([4], np.int8), 0), (np.array([7], np.int8), 1)):
+        assert lib.apmoe_plan_online(2, 4, lv.ctypes.data, hm.ctypes.data, nb.ctypes.data, fl.ctypes.data, n,
+                                     sb.ctypes.data, 2000, 0, 0, now.ctypes.data, out.ctypes.data,
+                                     ctypes.byref(stage)) == _lib.EINVAL
     # permute
     assert lib.apmoe_permute(fake, 4, 0, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
     assert lib.apmoe_permute(None, 4, 2, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL

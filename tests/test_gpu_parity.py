@@ -161,6 +161,34 @@ def test_route_stats(name):
     assert abs(float(mass.sum()) - cfg.T) <= 1e-4 * cfg.T
 
 
+def test_online_planner_commits_take_effect():
+    """An online re-plan under a growing KV footprint is committed in stream
+    order: the next forward call runs at the new bitwidths (checked against
+    the oracle at those bitwidths)."""
+    import torch
+    from any_precision_quantized_amd import layer as L
+    cfg = SMALL["ragged"]
+    inp = G.inputs(cfg)
+    bits0 = [6] * cfg.E
+    layer = L.from_inputs(inp, bits=bits0)
+    levels = [6, 5, 4, 3]
+    nbytes = np.array([[synth_bytes(cfg, b) for b in levels]] * cfg.E, dtype=np.uint64)
+    harm = np.array([[0.0, 1.0, 3.0, 7.0]] * cfg.E) * (1 + np.arange(cfg.E))[:, None]
+    planner_ = L.OnlinePlanner(layer, levels, harm, nbytes, [3] * cfg.E, [5, 4, 3],
+                               m_total=int(nbytes[:, 0].sum()), hysteresis=0, bits_now=bits0)
+    st, bits, stage, changed = planner_.step(m_kv=int(nbytes[0, 0] - nbytes[0, 2]) * 2)
+    assert st == _lib.OK and changed and stage >= 0
+    _, got = G.run_layer(inp, bits, layer=layer)
+    ref = moe.layer(inp, bits=bits)
+    assert np.array_equal(layer.bits.cpu().numpy(), np.asarray(bits, np.int8))
+    G.check_out(got, ref)
+
+
+def synth_bytes(cfg, b):
+    """Plane + LUT bytes of one expert's three matrices at b bits."""
+    return 3 * (cfg.H * cfg.I * b // 8) + (2 * cfg.I + cfg.H) * (1 << b) * 2
+
+
 @pytest.mark.parametrize("rows,cols", [(16, 32), (32, 704), (48, 320), (64, 4096)])
 def test_pack_planes_layout(rows, cols):
     """Packed word [p][group][step][g][i] is canonical word 4*step + g of row

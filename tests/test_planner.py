@@ -225,3 +225,29 @@ def test_online_first_feasible_stage_is_chosen():
             assert planner.plan_total(levels, nbytes, bits) <= budget
         else:
             assert st == planner.ENOSPACE
+
+
+def test_native_online_step_matches_oracle():
+    """apmoe_plan_online against the oracle step, bit-exact, over random
+    scenarios including a KV budget that grows and shrinks across steps."""
+    from any_precision_quantized_amd import _lib
+    rng = np.random.default_rng(21)
+    levels = np.array([6, 5, 4, 3], np.int8)
+    for trial in range(40):
+        E = int(rng.integers(1, 9))
+        harm = np.sort(rng.uniform(0, 1, size=(E, 4)), axis=1)
+        harm[:, 0] = 0.0
+        nbytes = np.sort(rng.integers(100, 1000, size=(E, 4)), axis=1)[:, ::-1].astype(np.uint64)
+        nbytes[:, 1:] = np.minimum(nbytes[:, 1:], nbytes[:, :-1] - 1)
+        floors = rng.choice([3, 4, 5], size=E).astype(np.int8)
+        stages = np.array([5, 4, 3], np.int8) if trial % 2 else np.array([4, 3], np.int8)
+        m_total = int(nbytes[:, 0].sum())
+        hyst = int(rng.integers(0, 200))
+        now = np.full(E, 6, np.int8)
+        for m_kv in np.concatenate([np.linspace(0, m_total, 7), np.linspace(m_total, 0, 7)]).astype(np.int64):
+            st, bits, stage = _lib.plan_online(levels, harm, nbytes, floors, stages, m_total, int(m_kv), hyst, now)
+            rst, rbits, rstage, _ = planner.online_step(levels, harm, nbytes, floors, stages, m_total, int(m_kv),
+                                                       hyst, now)
+            assert st == rst and stage == rstage, (trial, m_kv)
+            assert bits.tolist() == rbits.tolist(), (trial, m_kv)
+            now = bits
