@@ -205,9 +205,10 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
 
 // Routing statistics (the planner's online inputs).  norms_kernel: one wave
 // per token, ||x_t||_2 with the squares summed in fp32 and met in a fixed
-// butterfly.  stats_kernel: one wave per expert scans the T*k slots (lane l
-// takes slots l, l + 64, ...) adding its gates and gate * norm in fp32; the
-// lanes meet in a fixed butterfly, so the sums never depend on scheduling.
+// butterfly.  stats_kernel: one 16-wave workgroup per expert scans the T*k
+// slots (thread i takes slots i, i + 1024, ...) adding its gates and gate *
+// norm in fp32; lanes meet in a fixed butterfly and the 16 waves in index
+// order, so the sums never depend on scheduling.
 __global__ __launch_bounds__(4 * kWave) void norms_kernel(const half_t* __restrict__ x, int T, int H,
                                                           float* __restrict__ norms) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -224,26 +225,50 @@ __global__ __launch_bounds__(4 * kWave) void norms_kernel(const half_t* __restri
     if (lane == 0) norms[t] = sqrtf(acc);
 }
 
-__global__ __launch_bounds__(4 * kWave) void stats_kernel(const int32_t* __restrict__ ids,
-                                                          const float* __restrict__ w, int S, int k,
-                                                          const float* __restrict__ norms, int E,
-                                                          float* __restrict__ mass, float* __restrict__ wnorm) {
+constexpr int kStatWaves = 16;
+constexpr int kStatThreads = kStatWaves * kWave;
+constexpr int kStatUnroll = 4;
+
+__global__ __launch_bounds__(kStatThreads) void stats_kernel(const int32_t* __restrict__ ids,
+                                                             const float* __restrict__ w, int S, int k,
+                                                             const float* __restrict__ norms,
+                                                             float* __restrict__ mass, float* __restrict__ wnorm) {
+    __shared__ float part[2][kStatWaves];
+    const int e = blockIdx.x;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int e = blockIdx.x * 4 + wave;
-    if (e >= E) return;   // uniform over the wave; no barrier follows
     float m = 0.f, n = 0.f;
-    for (int s = lane; s < S; s += kWave) {
-        if (ids[s] == e) {
-            const float g = w[s];
-            m += g;
-            n = fmaf(g, norms[s / k], n);
+    for (int s0 = threadIdx.x; s0 < S; s0 += kStatUnroll * kStatThreads) {
+        int id[kStatUnroll];   // the unrolled id loads are independent, so they overlap
+#pragma unroll
+        for (int u = 0; u < kStatUnroll; ++u) {
+            const int s = s0 + u * kStatThreads;
+            id[u] = s < S ? ids[s] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kStatUnroll; ++u) {
+            const int s = s0 + u * kStatThreads;
+            if (id[u] == e) {
+                const float g = w[s];
+                m += g;
+                n = fmaf(g, norms[s / k], n);
+            }
         }
     }
     m = wave_sum(m);
     n = wave_sum(n);
     if (lane == 0) {
-        mass[e] = m;
-        wnorm[e] = n;
+        part[0][wave] = m;
+        part[1][wave] = n;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float sm = 0.f, sn = 0.f;
+        for (int v = 0; v < kStatWaves; ++v) {
+            sm += part[0][v];
+            sn += part[1][v];
+        }
+        mass[e] = sm;
+        wnorm[e] = sn;
     }
 }
 
@@ -321,7 +346,7 @@ extern "C" int apmoe_route_stats(const uint16_t* x, int T, int H, const int32_t*
         const int rc = launch_status();
         if (rc != APMOE_OK) return rc;
     }
-    hipLaunchKernelGGL(stats_kernel, dim3((E + 3) / 4), dim3(4 * kWave), 0, s, topk_ids, topk_w, T * k, k, norms, E,
-                       mass, wnorm);
+    hipLaunchKernelGGL(stats_kernel, dim3(E), dim3(kStatThreads), 0, s, topk_ids, topk_w, T * k, k, norms, mass,
+                       wnorm);
     return launch_status();
 }
