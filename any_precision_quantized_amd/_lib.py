@@ -22,7 +22,7 @@ GATE_UP_SWIGLU, DOWN = 0, 1
 ONLY_GEMV, ONLY_TILE = 0x10, 0x20
 MAX_EXPERTS = 256
 
-_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_c_int, _c_size, _vp, _u64 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint64
 
 
 class ApmoeError(RuntimeError):
@@ -58,6 +58,16 @@ def _lib():
             "apmoe_packed_plane_words": [_c_int, _c_int],
             "apmoe_pack_planes": [_vp, _c_int, _c_int, _vp, _vp],
             "apmoe_strerror": [_c_int],
+            "apmoe_arena_create": [_u64, _vp],
+            "apmoe_arena_alloc": [_vp, _u64, _vp],
+            "apmoe_arena_take": [_vp, _u64, _u64],
+            "apmoe_arena_release": [_vp, _u64, _u64],
+            "apmoe_arena_stats": [_vp, _vp, _vp, _vp],
+            "apmoe_pager_create": [_c_int, _c_int, _c_int, _vp, _vp, _vp, _u64, _vp, _vp, _vp],
+            "apmoe_pager_stage": [_vp, _vp, _vp],
+            "apmoe_pager_commit": [_vp, _vp],
+            "apmoe_pager_stats": [_vp, _vp, _vp, _vp, _vp, _vp],
+            "apmoe_pager_destroy": [_vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -66,6 +76,8 @@ def _lib():
         lib.apmoe_workspace_bytes.restype = _c_size
         lib.apmoe_packed_plane_words.restype = _c_size
         lib.apmoe_strerror.restype = ctypes.c_char_p
+        lib.apmoe_arena_destroy.argtypes = [_vp]
+        lib.apmoe_arena_destroy.restype = None
         _LIB = lib
     return _LIB
 
@@ -73,7 +85,7 @@ def _lib():
 def header_symbols():
     """Entry points declared in include/apmoe.h."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(apmoe_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|void|size_t|const char\*)\s+(apmoe_\w+)\s*\(", text, re.M)))
 
 
 def strerror(code: int) -> str:
@@ -256,3 +268,108 @@ def plan_online(levels, harm, nbytes, floor_bits, stage_bits, m_total, m_kv, hys
     if rc not in (OK, ENOSPACE):
         _check(rc, "apmoe_plan_online")
     return rc, out, stage.value
+
+
+# ---------------------------------------------------------------------------
+# Plane paging: the host-side arena allocator and the pager
+# ---------------------------------------------------------------------------
+
+class Arena:
+    """apmoe_arena_*: first-fit over [0, nbytes) in 256-byte units (host only)."""
+
+    def __init__(self, nbytes: int):
+        h = _vp()
+        _check(_lib().apmoe_arena_create(int(nbytes), ctypes.byref(h)), "apmoe_arena_create")
+        self._h = h
+
+    def alloc(self, nbytes: int):
+        """Offset of the new range, or None when no free range holds it."""
+        off = ctypes.c_uint64()
+        rc = _lib().apmoe_arena_alloc(self._h, int(nbytes), ctypes.byref(off))
+        if rc == ENOSPACE:
+            return None
+        _check(rc, "apmoe_arena_alloc")
+        return off.value
+
+    def take(self, off: int, nbytes: int) -> bool:
+        rc = _lib().apmoe_arena_take(self._h, int(off), int(nbytes))
+        if rc == ENOSPACE:
+            return False
+        _check(rc, "apmoe_arena_take")
+        return True
+
+    def release(self, off: int, nbytes: int) -> int:
+        return _lib().apmoe_arena_release(self._h, int(off), int(nbytes))
+
+    def stats(self):
+        """(free bytes, largest free range, number of free ranges)."""
+        f, l, n = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_int()
+        _check(_lib().apmoe_arena_stats(self._h, ctypes.byref(f), ctypes.byref(l), ctypes.byref(n)),
+               "apmoe_arena_stats")
+        return f.value, l.value, n.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _LIB is not None:
+            _LIB.apmoe_arena_destroy(h)
+            self._h = None
+
+
+class Pager:
+    """apmoe_pager_*: residency of E experts' planes and LUTs in a device arena.
+
+    host_planes / host_luts: host tensors (pinned) as the C ABI describes;
+    they are kept referenced here for the pager's lifetime."""
+
+    def __init__(self, E, H, I, host_planes, host_luts, arena, desc, bits):
+        torch = _torch()
+        assert len(host_planes) == 3 * E and len(host_luts) == 12 * E
+        for t in list(host_planes) + list(host_luts):
+            if t.device.type != "cpu" or not t.is_contiguous():
+                raise TypeError("host copies must be contiguous host tensors")
+        self._keep = (list(host_planes), list(host_luts), arena, desc, bits)
+        self.E = E
+        hp = (_vp * (3 * E))(*[t.data_ptr() for t in host_planes])
+        hl = (_vp * (12 * E))(*[t.data_ptr() for t in host_luts])
+        h = _vp()
+        rc = _lib().apmoe_pager_create(E, H, I, hp, hl, _ptr(arena, torch.uint8, None, "arena"), arena.numel(),
+                                       _ptr(desc, None, None, "desc"), _ptr(bits, torch.int8, E, "bits"),
+                                       ctypes.byref(h))
+        _check(rc, "apmoe_pager_create")
+        self._h = h
+
+    def stage(self, bits_new, copy_stream=None) -> int:
+        """Returns OK or ENOSPACE (nothing staged); raises on other errors."""
+        import numpy as np
+        b = np.ascontiguousarray(np.asarray(bits_new, dtype=np.int8))
+        if b.size != self.E:
+            raise ValueError(f"bits: expected {self.E} entries")
+        rc = _lib().apmoe_pager_stage(self._h, b.ctypes.data, _stream(copy_stream))
+        if rc == ENOSPACE:
+            return rc
+        _check(rc, "apmoe_pager_stage")
+        return rc
+
+    def commit(self, stream=None):
+        _check(_lib().apmoe_pager_commit(self._h, _stream(stream)), "apmoe_pager_commit")
+
+    def stats(self):
+        """dict: resident, free, largest_free, h2d, d2d (bytes)."""
+        v = [ctypes.c_uint64() for _ in range(5)]
+        _check(_lib().apmoe_pager_stats(self._h, *[ctypes.byref(x) for x in v]), "apmoe_pager_stats")
+        return dict(zip(("resident", "free", "largest_free", "h2d", "d2d"), (x.value for x in v)))
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _LIB is not None:
+            self._h = None
+            _check(_LIB.apmoe_pager_destroy(h), "apmoe_pager_destroy")
+
+    def __del__(self):
+        import sys
+        if sys.is_finalizing():   # the HIP runtime may already be gone
+            return
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -36,7 +36,6 @@ namespace apmoe {
 namespace {
 
 constexpr int kThreadsTile = 512;
-constexpr int kTRows = 256;              // weight rows per tile (gate/up: 128 + 128)
 constexpr int kTToks = 256;              // tokens per tile
 constexpr int kRowB = 80;                // LDS bytes per tile row: 32 halves + 16 pad
 constexpr int kTileB = 256 * kRowB;
@@ -111,7 +110,8 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
     const int rowc = min(r0 + tr % kMatRows, rows - 1);
     const apmoe_mat& mt = NMAT == 2 ? (hsel ? a.experts[it.e].up : a.experts[it.e].gate) : a.experts[it.e].down;
     const MatView mv = mat_view(mt, it.b);
-    const uint32_t pbytes = 6u * (uint32_t)rows * 16u * (uint32_t)nsteps128;
+    // the resource covers the b resident planes only (none at 16 bits)
+    const uint32_t pbytes = (uint32_t)(it.b <= kPlanes ? it.b : 0) * (uint32_t)rows * 16u * (uint32_t)nsteps128;
     const uint32_t slab = (uint32_t)rows * 16u * (uint32_t)nsteps128;
     const uint32_t wbytes = (uint32_t)rows * (uint32_t)K * 2u;
 

@@ -510,7 +510,8 @@ void gemv_kernel(GemmArgs a, int KS, float* partial) {
     mv.planes[1] = (const void*)v1.planes;
     mv.w16[0] = (const void*)v0.w16;
     mv.w16[1] = (const void*)v1.w16;
-    mv.pbytes = 6u * (uint32_t)sh.rows * 16u * (uint32_t)sh.nsteps;
+    // the resource covers the b resident planes only (none at 16 bits)
+    mv.pbytes = (uint32_t)(it.b <= kPlanes ? it.b : 0) * (uint32_t)sh.rows * 16u * (uint32_t)sh.nsteps;
     mv.wbytes = (uint32_t)sh.rows * (uint32_t)sh.K * 2u;
 
     switch (it.b) {
@@ -548,9 +549,12 @@ __device__ __forceinline__ void finalize_rows(const GemmArgs& a, int KS, const f
 
 // Sum the K-split partials in split order (SwiGLU for gate/up).  Workgroup
 // (x, y) takes positions [x * pb, (x + 1) * pb) and rows [1024 y, 1024 y +
-// 1024), four rows per thread; positions of tile-path groups are left alone,
-// so a launch whose groups all took the tile path costs about a thousand
-// short workgroups.  pb is chosen on the host to keep the grid near that.
+// 1024), four rows per thread.  Positions are grouped by expert, so the
+// workgroup finds the expert of its first position once and then walks expert
+// ranges, skipping a whole range when that group took the tile path (or has
+// no bit-plane or fp16 weights); a launch whose groups all took the tile path
+// costs one lookup per workgroup.  pb is chosen on the host to keep the grid
+// near a thousand workgroups.
 constexpr int kFinRows = 4 * 256;
 template <int NMAT>
 __global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, const float* partial, int pb) {
@@ -560,16 +564,21 @@ __global__ __launch_bounds__(256) void gemv_finalize_kernel(GemmArgs a, int KS, 
     const int rows = NMAT == 2 ? a.I : a.H;
     const int S = a.T * a.k;
     const int row = blockIdx.y * kFinRows + 4 * threadIdx.x;
-    const int pend = min(S, (blockIdx.x + 1) * pb);
-    for (int p = blockIdx.x * pb; p < pend; ++p) {
-        int lo = 0, hi = a.E - 1;   // expert holding position p: last e with offs[e] <= p
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (offs[mid] <= p) lo = mid; else hi = mid - 1;
-        }
-        const int m = offs[lo + 1] - offs[lo];
-        if (m >= a.mfma_min_tokens || !valid_bits(a.bits[lo])) continue;   // uniform over the workgroup
-        if (row < rows) finalize_rows<NMAT>(a, KS, partial, S, rows, p, row);
+    int p = blockIdx.x * pb;
+    const int pend = min(S, p + pb);
+    if (p >= pend) return;   // uniform over the workgroup
+    int lo = 0, hi = a.E - 1;   // expert holding position p: last e with offs[e] <= p
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offs[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    // offs[lo] <= p < offs[lo + 1]; offs[E] = S >= pend ends the walk at e = E - 1
+    for (int e = lo; p < pend; ++e) {
+        const int eend = min(pend, offs[e + 1]);
+        const int m = offs[e + 1] - offs[e];
+        if (m < a.mfma_min_tokens && valid_bits(a.bits[e]) && row < rows)
+            for (; p < eend; ++p) finalize_rows<NMAT>(a, KS, partial, S, rows, p, row);
+        p = eend;
     }
 }
 

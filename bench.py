@@ -112,6 +112,84 @@ def counted_traffic(kernel):
     return None
 
 
+def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
+    """Throughput while a re-plan's plane copies run (plane paging).
+
+    A second layer runs on paged weights (PagedExperts).  Each repetition
+    demotes every bit-plane expert above 3 bits by one bit (committed, so only
+    the lower LUTs move), then enqueues `steps` layer steps, stages the
+    promotion back to `bits` (host-to-device plane and LUT copies on the copy
+    stream, issued while those steps run), enqueues `steps` more and commits.
+    Per-step events give the steps that overlapped the copy window; their
+    mean time against an idle run's is the loss."""
+    import numpy as np
+    import torch
+    from any_precision_quantized_amd import _lib
+    from any_precision_quantized_amd import layer as L
+    from any_precision_quantized_amd.paging import PagedExperts, arena_bytes_for
+
+    pe = PagedExperts(inp.experts, cfg.H, cfg.I, arena_bytes_for(cfg.H, cfg.I, cfg.E))
+    shared = L.ExpertTable([inp.shared]) if inp.shared is not None else None
+    lay = L.MoELayer(cfg.E, cfg.H, cfg.I, cfg.k, cfg.T, inp.w_router, inp.bias, cfg.logit_scale, pe.table, bits,
+                     shared, cfg.shared_I, mfma_min)
+    pe.attach(lay, bits)
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
+    stream = torch.cuda.current_stream()
+    low = np.where((bits > 3) & (bits <= 6), bits - 1, bits).astype(np.int8)
+
+    def enqueue(n, evs):
+        for _ in range(n):
+            lay.forward(x)
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            evs.append(e)
+
+    def step_us(evs):
+        return [a.elapsed_time(b) * 1e3 for a, b in zip(evs[:-1], evs[1:])]
+
+    for _ in range(10):
+        lay.forward(x)
+    torch.cuda.synchronize()
+    evs = []
+    enqueue(2 * steps + 1, evs)
+    torch.cuda.synchronize()
+    idle = step_us(evs)
+    during, copy_ms, h2d, d2d = [], [], 0, 0
+    for _ in range(reps):
+        if pe.apply(low) != _lib.OK:
+            raise RuntimeError("paging probe: demotion did not fit")
+        torch.cuda.synchronize()
+        evs = []
+        enqueue(steps + 1, evs)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(pe.copy_stream)
+        if pe.stage(bits) != _lib.OK:
+            raise RuntimeError("paging probe: promotion did not fit")
+        c1.record(pe.copy_stream)
+        enqueue(steps, evs)
+        pe.commit(bits)
+        torch.cuda.synchronize()
+        st = pe.stats()
+        h2d, d2d = st["h2d"], st["d2d"]
+        lo, hi = evs[0].elapsed_time(c0), evs[0].elapsed_time(c1)
+        copy_ms.append(hi - lo)
+        for i, us in enumerate(step_us(evs)):
+            a, b = evs[0].elapsed_time(evs[i]), evs[0].elapsed_time(evs[i + 1])
+            if b > lo and a < hi:
+                during.append(us)
+    pe.close()
+    idle_us = float(np.mean(idle))
+    during_us = float(np.mean(during)) if during else None
+    cm = float(np.mean(copy_ms))
+    return {"replan": "every bit-plane expert above 3 bits promoted by one plane (b-1 -> b) while the layer runs",
+            "h2d_bytes": int(h2d), "d2d_bytes": int(d2d), "copy_ms": round(cm, 3),
+            "h2d_GBps": round(h2d / (cm * 1e-3) / 1e9, 2) if cm > 0 else None,
+            "step_us_idle": round(idle_us, 2),
+            "step_us_during_copy": None if during_us is None else round(during_us, 2),
+            "steps_overlapping_copy": len(during),
+            "loss": None if during_us is None else round(during_us / idle_us - 1.0, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +198,8 @@ def main():
     ap.add_argument("--workload", default="qwen_decode")
     ap.add_argument("--mfma-min-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paging-probe", action="store_true",
+                    help="skip the throughput-under-plane-paging probe")
     ap.add_argument("--serial-shared", action="store_true",
                     help="run the shared expert on the main stream instead of the side stream")
     ap.add_argument("--replica-bytes", type=float, default=1.0e9,
@@ -338,6 +418,9 @@ def main():
         "route_stats_us": round(route_stats_us, 2),
         "per_launch_bytes": {n: int(by.get(n, 0)) for n in names},
     }
+    if not args.no_paging_probe:
+        del tables, shared, steps
+        result["paging"] = paging_probe(cfg, inp, bits, mfma_min)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, bits)
     print(json.dumps(result), flush=True)

@@ -249,6 +249,83 @@ int apmoe_pack_planes(const uint32_t* src, int rows, int cols, uint32_t* dst, vo
 /* Static description of an error code. */
 const char* apmoe_strerror(int code);
 
+/*
+ * Plane paging ("内存的饥饿游戏：当 MoE 权重与 KV 缓存争夺 GPU 的每一字节",
+ * zhichai.net, sections "核心洞察：权重也能分页" and "安全边界与异步搬运": the
+ * bit-planes are the pages, moved between GPU and host asynchronously and
+ * committed at a safe boundary so that the movement hides behind inference).
+ *
+ * apmoe_arena_*: a host-side first-fit allocator over an address range
+ * [0, bytes) in 256-byte units; it never touches memory, so it runs without a
+ * GPU.  Free ranges are kept coalesced.
+ *  create   bytes rounded down to 256; *out owned by the caller (destroy).
+ *  alloc    first free range (lowest offset) that holds bytes (rounded up to
+ *           256); APMOE_ENOSPACE if none.
+ *  take     claim exactly [off, off + bytes) if all of it is free, else
+ *           APMOE_ENOSPACE; off must be 256-aligned.
+ *  release  return [off, off + bytes); APMOE_EINVAL (and no change) if any
+ *           of it lies outside the range or is already free.
+ *  stats    free bytes, largest free range, number of free ranges (any may be NULL).
+ */
+typedef struct apmoe_arena apmoe_arena;
+int apmoe_arena_create(uint64_t bytes, apmoe_arena** out);
+void apmoe_arena_destroy(apmoe_arena* arena);
+int apmoe_arena_alloc(apmoe_arena* arena, uint64_t bytes, uint64_t* off);
+int apmoe_arena_take(apmoe_arena* arena, uint64_t off, uint64_t bytes);
+int apmoe_arena_release(apmoe_arena* arena, uint64_t off, uint64_t bytes);
+int apmoe_arena_stats(const apmoe_arena* arena, uint64_t* free_bytes, uint64_t* largest, int* n_ranges);
+
+/*
+ * apmoe_pager_*: residency of E experts' bit-planes and LUTs in a device
+ * arena.  An expert at b in {3..6} bits holds planes 0..b-1 of each of its
+ * three matrices (one block per matrix, planes at the packed slab stride, so
+ * the GEMM's addressing is unchanged) and the b-bit LUT of each; at 16 bits
+ * it holds neither (its fp16 weights, which the caller places in the
+ * descriptors, are not paged).
+ *  create  host_planes [3E]: per expert gate, up, down, the six packed slabs
+ *          (apmoe_packed_plane_words(rows, cols) words, as apmoe_pack_planes
+ *          writes them); host_luts [3E][4]: fp16 [rows][1 << b] for b = 3..6.
+ *          Host memory that must outlive the pager and stay unchanged; it
+ *          should be pinned (hipHostMalloc) so the copies run asynchronously.
+ *          arena: device memory (256-byte aligned, arena_bytes) owned by the
+ *          caller; the pager keeps a patch buffer in it.  experts: the device
+ *          descriptors of these E experts (gate/up/down planes and lut words
+ *          are written by commits; w16 words are left alone); bits: their
+ *          device bits table.  Nothing is resident until the first commit.
+ *          APMOE_ENOSPACE if the arena cannot hold the patch buffer.
+ *  stage   bits_new [E] (host): enqueue on copy_stream the copies that make
+ *          the new residency (host-to-device copies of the planes and LUTs
+ *          that become resident; a block that cannot grow in place is moved,
+ *          its resident planes copied device to device) and record what the
+ *          commit retires.  The layer keeps running at the old bitwidths
+ *          meanwhile.  APMOE_EBITS for a bitwidth outside {3,4,5,6,16};
+ *          APMOE_ENOSPACE (nothing staged, nothing enqueued) when the arena
+ *          cannot hold the new blocks even after waiting for retired blocks;
+ *          APMOE_EINVAL if a staged change is not yet committed.  Waits on the
+ *          host for the previous commit to have executed.
+ *  commit  on stream: wait for the staged copies, then write the plane and
+ *          LUT pointers of every paged matrix and the bits table together
+ *          (one kernel), so every later kernel on stream sees the new
+ *          bitwidths and every earlier one the old.  Blocks the change retires
+ *          return to the arena once the stream has passed the commit.  All
+ *          kernels that read these experts must be ordered on stream.
+ *  stats   resident plane and LUT bytes, arena free bytes and largest free
+ *          range, and the bytes the last stage copied host to device and
+ *          device to device (any pointer may be NULL).
+ *  destroy waits for outstanding copies and commits; the arena stays the
+ *          caller's.
+ * Needs 1 <= E <= APMOE_MAX_EXPERTS, H % 32 == 0, I % 32 == 0.
+ */
+typedef struct apmoe_pager apmoe_pager;
+int apmoe_pager_create(int E, int H, int I, const void* const* host_planes, const void* const* host_luts,
+                       void* arena, uint64_t arena_bytes, apmoe_expert* experts, int8_t* bits,
+                       apmoe_pager** out);
+int apmoe_pager_stage(apmoe_pager* pager, const int8_t* bits_new, void* copy_stream);
+int apmoe_pager_commit(apmoe_pager* pager, void* stream);
+int apmoe_pager_stats(apmoe_pager* pager, uint64_t* resident_bytes, uint64_t* free_bytes,
+                      uint64_t* largest_free, uint64_t* h2d_bytes, uint64_t* d2d_bytes);
+int apmoe_pager_destroy(apmoe_pager* pager);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,184 @@
+"""Plane paging on the GPU through the C ABI (apmoe_pager_*).
+
+After every staged and committed change of bitwidths the layer's output is
+checked against the oracle at the new bitwidths (the layer bar), the resident
+blocks are read back and compared bit for bit with the host copy (the top b
+packed planes and the b-bit LUT of every matrix, no other pointer set), and
+the resident and host-to-device bytes are compared with the paging oracle.
+"""
+import numpy as np
+import pytest
+
+import synth
+from any_precision_quantized_amd import _lib
+from any_precision_quantized_amd.layer import MATS, ExpertTable, MoELayer
+from any_precision_quantized_amd.paging import PagedExperts, arena_bytes_for
+from oracle import moe, paging
+
+from . import gpu_helpers as G
+from .oracle_cache import layer_ref, resolve_bits
+
+pytestmark = pytest.mark.gpu
+
+# K of every matrix a multiple of 128, so packed slabs hold no padding and the
+# byte counts equal the oracle's; expert 4 has fp16 weights and may run at 16 bits
+PAGED = synth.custom("paged", E=6, H=256, I=384, k=2, T=40, bits=(3, 4, 5, 6, 16, 4))
+RAGGED = synth.custom("ragged", E=6, H=320, I=416, k=2, T=37, bits=(3, 4, 5, 6, 16, 4))
+PLANS = [
+    [6, 6, 6, 6, 16, 6],     # promote everything
+    [3, 3, 3, 3, 16, 3],     # demote everything (LUTs change, no plane moves)
+    [5, 3, 6, 4, 6, 3],      # mixed; expert 4 from the fp16 fallback to 6 bit-planes
+    [4, 6, 3, 5, 16, 5],
+]
+
+
+def _paged(cfg, bits0, arena_bytes=None):
+    import torch
+    inp = G.inputs(cfg)
+    pe = PagedExperts(inp.experts, cfg.H, cfg.I,
+                      arena_bytes if arena_bytes is not None else arena_bytes_for(cfg.H, cfg.I, cfg.E))
+    shared = ExpertTable([inp.shared]) if inp.shared is not None else None
+    layer = MoELayer(cfg.E, cfg.H, cfg.I, cfg.k, cfg.T, inp.w_router, inp.bias, cfg.logit_scale, pe.table,
+                     bits0, shared, cfg.shared_I)
+    pe.attach(layer, bits0)
+    torch.cuda.synchronize()
+    return inp, pe, layer
+
+
+def _forward(inp, layer):
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
+    out = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _check_resident(pe, layer, bits):
+    """Descriptor words of every paged matrix point into the arena at blocks
+    that hold exactly the host copy's top b planes and b-bit LUT."""
+    import torch
+    torch.cuda.synchronize()
+    n = layer.n_shared
+    desc = layer.table.desc[n:].cpu().numpy().astype(np.uint64)
+    dbits = layer.bits[n:].cpu().numpy()
+    assert dbits.tolist() == [int(b) for b in bits]
+    arena = pe.arena.cpu().numpy()
+    base = pe.arena.data_ptr()
+    for e, b in enumerate(bits):
+        b = int(b)
+        for j, name in enumerate(MATS):
+            words = desc[e, 6 * j: 6 * j + 6]
+            w16 = pe.table.tensors[e][name]["w16"]
+            assert int(words[5]) == (0 if w16 is None else w16.data_ptr()), "w16 word left alone"
+            if b == 16:
+                assert words[:5].tolist() == [0] * 5
+                continue
+            host = pe.host_planes[3 * e + j].numpy().view(np.uint8)
+            slab = host.size // 6
+            off = int(words[0]) - base
+            assert 0 <= off and off + b * slab <= arena.size and off % 256 == 0
+            assert np.array_equal(arena[off:off + b * slab], host[:b * slab]), f"planes of expert {e} {name}"
+            for bb in range(3, 7):
+                if bb != b:
+                    assert int(words[1 + bb - 3]) == 0
+            lut = pe.host_luts[4 * (3 * e + j) + b - 3].numpy().view(np.uint8).reshape(-1)
+            lo = int(words[1 + b - 3]) - base
+            assert 0 <= lo and lo + lut.size <= arena.size and lo % 256 == 0
+            assert np.array_equal(arena[lo:lo + lut.size], lut), f"LUT of expert {e} {name}"
+
+
+@pytest.mark.parametrize("cfg", [PAGED, RAGGED], ids=lambda c: c.name)
+def test_paged_layer_follows_every_plan(cfg):
+    G.say(f"paged layer {cfg.name}")
+    bits0 = list(cfg.bits)
+    inp, pe, layer = _paged(cfg, bits0)
+    exact = cfg.H % 128 == 0 and cfg.I % 128 == 0
+    prev = bits0
+    for bits in [bits0] + PLANS:
+        if bits is not bits0:
+            assert pe.apply(bits) == _lib.OK
+        st = pe.stats()
+        if exact:
+            assert st["resident"] == paging.resident_bytes(cfg.H, cfg.I, bits)
+            if bits is not bits0:
+                assert st["h2d"] == paging.host_to_device_bytes(cfg.H, cfg.I, prev, bits)
+        if bits is PLANS[0]:
+            assert st["d2d"] > 0, "blocks packed back to back: a promotion moves them"
+        _check_resident(pe, layer, bits)
+        got = _forward(inp, layer)
+        G.check_out({"out": got}, moe.layer(inp, bits=np.asarray(bits, np.int8)))
+        G.say(f"  bits {bits}: resident {st['resident']} h2d {st['h2d']} d2d {st['d2d']}")
+        prev = bits
+    pe.close()
+
+
+def test_paging_grows_in_place_after_retire():
+    """A demotion's tails return to the arena once the stream has passed its
+    commit; promoting back then grows every block in place (no device-to-device
+    move)."""
+    import torch
+    cfg = PAGED
+    inp, pe, layer = _paged(cfg, [6] * cfg.E)
+    assert pe.apply([3] * cfg.E) == _lib.OK
+    torch.cuda.synchronize()
+    assert pe.apply([6] * cfg.E) == _lib.OK
+    st = pe.stats()
+    assert st["d2d"] == 0 and st["h2d"] == paging.host_to_device_bytes(cfg.H, cfg.I, [3] * cfg.E, [6] * cfg.E)
+    _check_resident(pe, layer, [6] * cfg.E)
+    G.check_out({"out": _forward(inp, layer)}, moe.layer(inp, bits=np.full(cfg.E, 6, np.int8)))
+    pe.close()
+
+
+def test_paging_commit_in_stream_order():
+    """Copies staged, a forward call enqueued before the commit runs at the
+    old bitwidths, one enqueued after it at the new."""
+    import torch
+    cfg = PAGED
+    inp, pe, layer = _paged(cfg, list(cfg.bits))
+    old, new = list(cfg.bits), [6, 6, 6, 6, 6, 6]
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
+    assert pe.stage(new) == _lib.OK
+    out1 = layer.forward(x).clone()
+    pe.commit(new)
+    out2 = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    G.check_out({"out": out1.float().cpu().numpy()}, moe.layer(inp, bits=np.asarray(old, np.int8)))
+    G.check_out({"out": out2.float().cpu().numpy()}, moe.layer(inp, bits=np.asarray(new, np.int8)))
+    _check_resident(pe, layer, new)
+    pe.close()
+
+
+def test_paging_enospace_keeps_the_plan():
+    """An arena that holds the 3-bit plan but not the 6-bit one: staging the
+    promotion fails with nothing changed, and the layer keeps its plan."""
+    cfg = PAGED
+    small = paging.resident_bytes(cfg.H, cfg.I, [3] * cfg.E) + 64 * 1024
+    inp, pe, layer = _paged(cfg, [3] * cfg.E, arena_bytes=small)
+    before = pe.stats()
+    assert pe.apply([6] * cfg.E) == _lib.ENOSPACE
+    after = pe.stats()
+    assert after["resident"] == before["resident"] and after["free"] == before["free"]
+    _check_resident(pe, layer, [3] * cfg.E)
+    G.check_out({"out": _forward(inp, layer)}, moe.layer(inp, bits=np.full(cfg.E, 3, np.int8)))
+    pe.close()
+
+
+def test_paged_qwen_decode_full_size():
+    """The Qwen-shaped decode layer (60 experts, four always-on fp16 experts
+    in front of them in the descriptor table) on paged weights, before and
+    after demoting the ten lowest-indexed 6-bit experts by one bit."""
+    cfg = synth.get("qwen_decode")
+    G.say("paged qwen_decode")
+    inp0 = G.inputs(cfg)
+    bits0 = resolve_bits(inp0)
+    inp, pe, layer = _paged(cfg, bits0)
+    assert layer.n_shared == 4
+    G.check_out({"out": _forward(inp, layer)}, layer_ref(inp, bits0))
+    bits1 = np.array(bits0, np.int8)
+    six = np.nonzero(bits1 == 6)[0][:10]
+    bits1[six] = 5
+    assert pe.apply(bits1) == _lib.OK
+    _check_resident(pe, layer, bits1)
+    G.check_out({"out": _forward(inp, layer)}, layer_ref(inp, bits1))
+    G.say(f"  demoted {len(six)} experts; {pe.stats()}")
+    pe.close()

@@ -1,7 +1,13 @@
-"""Pins of the paging oracle: hand-worked residency and copy bytes and a
-hand-worked first-fit sequence."""
-import numpy as np
+"""Plane paging on the CPU: pins of the paging oracle (hand-worked residency
+and copy bytes, a hand-worked first-fit sequence), the native arena allocator
+against the oracle's bitmap first-fit on seeded operation sequences, and the
+pager's argument checks (no GPU call is reached)."""
+import ctypes
 
+import numpy as np
+import pytest
+
+from any_precision_quantized_amd import _lib
 from oracle import paging
 
 
@@ -63,3 +69,101 @@ def test_first_fit_hand_sequence():
     assert not a.release(256, 512)             # partly free
     assert a.take(1792, 256) and not a.take(1792, 256)
     assert a.take(0, 300) and a.stats() == (0, 0, 0)
+
+
+# ---------------------------------------------------------------------------
+# Native arena against the oracle
+# ---------------------------------------------------------------------------
+
+def _apply(arena, ff, op, arg):
+    if op == "alloc":
+        return arena.alloc(arg), ff.alloc(arg)
+    if op == "take":
+        off, n = arg
+        return arena.take(off, n), ff.take(off, n)
+    off, n = arg
+    return arena.release(off, n) == _lib.OK, ff.release(off, n)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_native_arena_matches_first_fit(seed):
+    rng = np.random.default_rng(seed)
+    size = 256 * int(rng.integers(16, 96))
+    arena, ff = _lib.Arena(size), paging.FirstFit(size)
+    live = []
+    for step in range(400):
+        r = rng.random()
+        if r < 0.45 or not live:
+            op, arg = "alloc", int(rng.integers(1, size // 6))
+        elif r < 0.8:
+            i = int(rng.integers(len(live)))
+            off, n = live[i]
+            if rng.random() < 0.3:       # part of a live range: the tail, as a demotion frees
+                cut = 256 * int(rng.integers(0, max(1, n // 256)))
+                op, arg = "release", (off + cut, n - cut)
+            else:
+                op, arg = "release", (off, n)
+        elif r < 0.9:
+            op, arg = "take", (256 * int(rng.integers(0, size // 256)), int(rng.integers(1, 1024)))
+        else:                            # a bad release: free memory or past the end
+            op, arg = "release", (256 * int(rng.integers(0, size // 256 + 2)), 256 * int(rng.integers(1, 6)))
+        got, want = _apply(arena, ff, op, arg)
+        assert got == want, (step, op, arg, got, want)
+        assert arena.stats() == ff.stats(), (step, op, arg)
+        if op == "alloc" and got is not None:
+            live.append((got, 256 * paging.FirstFit.units(arg)))
+        elif op == "release" and got:
+            off, n = arg
+            n = 256 * paging.FirstFit.units(n)
+            for j, (o, m) in enumerate(live):
+                if o <= off < o + m:
+                    live[j] = (o, off - o)
+                    if off - o == 0:
+                        live.pop(j)
+                    break
+        elif op == "take" and got:
+            live.append((arg[0], 256 * paging.FirstFit.units(arg[1])))
+
+
+def test_native_arena_argument_errors():
+    lib = _lib._lib()
+    a = _lib.Arena(4096)
+    off = ctypes.c_uint64()
+    assert lib.apmoe_arena_alloc(a._h, 0, ctypes.byref(off)) == _lib.EINVAL
+    assert lib.apmoe_arena_take(a._h, 100, 256) == _lib.EINVAL        # misaligned
+    assert lib.apmoe_arena_release(a._h, 4096, 256) == _lib.EINVAL    # past the end
+    assert lib.apmoe_arena_release(a._h, 0, 256) == _lib.EINVAL       # already free
+    assert lib.apmoe_arena_alloc(a._h, 8192, ctypes.byref(off)) == _lib.ENOSPACE
+    assert lib.apmoe_arena_create(4096, None) == _lib.EINVAL
+    assert a.stats() == (4096, 4096, 1)
+
+
+# ---------------------------------------------------------------------------
+# Pager argument checks (rejected before any GPU call)
+# ---------------------------------------------------------------------------
+
+def test_pager_create_argument_errors():
+    lib = _lib._lib()
+    E, H, I = 2, 64, 96
+    fake = ctypes.c_void_p(1 << 20)
+    hp = (ctypes.c_void_p * (3 * E))(*([1 << 20] * 3 * E))
+    hl = (ctypes.c_void_p * (12 * E))(*([1 << 20] * 12 * E))
+    out = ctypes.c_void_p()
+    big = 1 << 30
+    assert lib.apmoe_pager_create(0, H, I, hp, hl, fake, big, fake, fake, ctypes.byref(out)) == _lib.EINVAL
+    assert lib.apmoe_pager_create(E, 48, I, hp, hl, fake, big, fake, fake, ctypes.byref(out)) == _lib.EINVAL
+    assert lib.apmoe_pager_create(E, H, 80, hp, hl, fake, big, fake, fake, ctypes.byref(out)) == _lib.EINVAL
+    assert lib.apmoe_pager_create(E, H, I, None, hl, fake, big, fake, fake, ctypes.byref(out)) == _lib.EINVAL
+    assert lib.apmoe_pager_create(E, H, I, hp, hl, ctypes.c_void_p((1 << 20) + 64), big, fake, fake,
+                                  ctypes.byref(out)) == _lib.EINVAL     # arena not 256-aligned
+    hl_null = (ctypes.c_void_p * (12 * E))(*([1 << 20] * (12 * E - 1) + [None]))
+    assert lib.apmoe_pager_create(E, H, I, hp, hl_null, fake, big, fake, fake, ctypes.byref(out)) == _lib.EINVAL
+    assert lib.apmoe_pager_create(E, H, I, hp, hl, fake, big, fake, fake, None) == _lib.EINVAL
+    # the patch buffer (3E x 5 pointer patches and the bits) does not fit
+    assert lib.apmoe_pager_create(E, H, I, hp, hl, fake, 256, fake, fake, ctypes.byref(out)) == _lib.ENOSPACE
+    assert out.value is None
+    for fn in ("apmoe_pager_stage", "apmoe_pager_commit", "apmoe_pager_stats"):
+        args = {"apmoe_pager_stage": (None, None, None), "apmoe_pager_commit": (None, None),
+                "apmoe_pager_stats": (None, None, None, None, None, None)}[fn]
+        assert getattr(lib, fn)(*args) == _lib.EINVAL
+    assert lib.apmoe_pager_destroy(None) == _lib.OK
