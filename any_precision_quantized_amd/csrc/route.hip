@@ -71,8 +71,9 @@ __global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* _
 }
 
 // k rounds of a wave-wide argmax over v (lane's experts lane + 64c), ties to
-// the lower expert, then the softmax over the chosen logits in fp64; lane 0
-// writes the results of token t.  chosen: k doubles of LDS for this wave.
+// the lower expert, then the softmax over the chosen logits in fp64: lane j
+// takes the exponentials of chosen logits j, j + 64, ... and the wave adds
+// them in a fixed butterfly.  chosen: k doubles of LDS for this wave.
 template <int kPer>
 __device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int t, int lane, double* chosen,
                                             int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
@@ -94,17 +95,20 @@ __device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int
 #pragma unroll
         for (int c = 0; c < kPer; ++c)
             if (lane + kWave * c == best_e) v[c] = -__builtin_inf();
-        if (lane == 0) {
+        if (lane == (j & (kWave - 1))) {
             chosen[j] = best;
             topk_ids[(size_t)t * k + j] = best_e;
         }
     }
-    if (lane == 0) {
-        const double lmax = chosen[0];
-        double sum = 0.0;
-        for (int j = 0; j < k; ++j) sum += exp(chosen[j] - lmax);
-        for (int j = 0; j < k; ++j) topk_w[(size_t)t * k + j] = (float)(exp(chosen[j] - lmax) / sum);
-    }
+    // chosen[] was written by other lanes of this wave: order the reads after it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const double lmax = chosen[0];
+    double part = 0.0;
+    for (int j = lane; j < k; j += kWave) part += exp(chosen[j] - lmax);
+    const double sum = wave_sum(part);
+    for (int j = lane; j < k; j += kWave) topk_w[(size_t)t * k + j] = (float)(exp(chosen[j] - lmax) / sum);
 }
 
 // Fused router: TB tokens per workgroup, all E logits in LDS, then select.

@@ -37,6 +37,8 @@ SMALL = {
     "wide": synth.custom("wide", E=3, H=192, I=288, k=2, T=128, bits=(4, 6, 3)),
     # shared expert of 3x the routed size: three always-on experts in the routed launches
     "shared_fused": synth.custom("shared_fused", E=5, H=192, I=96, k=2, T=40, bits=(3, 4, 5, 6, 16), shared_I=288),
+    # two fp16 experts of 70 tokens each: on the GEMV path, token chunks of 32 + 32 + 6
+    "fp16_wide": synth.custom("fp16_wide", E=2, H=128, I=192, k=2, T=70, bits=(16, 16)),
     # shared expert whose size is no multiple of I: its own launches on a side stream
     "shared_side": synth.custom("shared_side", E=4, H=160, I=128, k=1, T=33, bits=(6, 3, 4, 5), shared_I=224),
 }
