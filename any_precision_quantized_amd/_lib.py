@@ -68,6 +68,9 @@ def _lib():
             "apmoe_pager_commit": [_vp, _vp],
             "apmoe_pager_stats": [_vp, _vp, _vp, _vp, _vp, _vp],
             "apmoe_pager_destroy": [_vp],
+            "apmoe_exp_plan": [_vp, _u64, _vp, _vp, _vp],
+            "apmoe_exp_encode": [_vp, _u64, _vp, _vp, _u64, _vp, _vp, _vp],
+            "apmoe_exp_decode": [_vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -373,3 +376,39 @@ class Pager:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------------------
+# Lossless exponent codec (fp16 weights)
+# ---------------------------------------------------------------------------
+
+def exp_encode(w16):
+    """Host encoder: w16 numpy uint16 [n] -> dict(lengths, words, block_off,
+    lo, table) of numpy arrays (the library's apmoe_exp_plan + _encode)."""
+    import numpy as np
+    w = np.ascontiguousarray(np.asarray(w16, dtype=np.uint16).reshape(-1))
+    n = w.size
+    lengths = np.zeros(256, dtype=np.uint8)
+    nwords, nblocks = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(_lib().apmoe_exp_plan(w.ctypes.data, n, lengths.ctypes.data, ctypes.byref(nwords),
+                                 ctypes.byref(nblocks)), "apmoe_exp_plan")
+    words = np.zeros(nwords.value, dtype=np.uint32)
+    offs = np.zeros(nblocks.value, dtype=np.uint32)
+    lo = np.zeros(n, dtype=np.uint8)
+    table = np.zeros(4096, dtype=np.uint16)
+    _check(_lib().apmoe_exp_encode(w.ctypes.data, n, lengths.ctypes.data, words.ctypes.data, words.size,
+                                   offs.ctypes.data, lo.ctypes.data, table.ctypes.data), "apmoe_exp_encode")
+    return {"lengths": lengths, "words": words, "block_off": offs, "lo": lo, "table": table, "n": n}
+
+
+def exp_decode(words, block_off, lo, table, out, stream=None):
+    """Device decoder: int32/uint8/int16 device tensors as exp_encode's arrays
+    (words int32 [nwords], block_off int32, lo uint8 [n], table int16 [4096]) ->
+    out int16 [n] (fp16 bit patterns)."""
+    torch = _torch()
+    n = out.numel()
+    rc = _lib().apmoe_exp_decode(_ptr(words, torch.int32, 2, "words"), words.numel(),
+                                 _ptr(block_off, torch.int32, None, "block_off"), _ptr(lo, torch.uint8, n, "lo"),
+                                 _ptr(table, torch.int16, 4096, "table"), n, _ptr(out, torch.int16, n, "out"),
+                                 _stream(stream))
+    _check(rc, "apmoe_exp_decode")

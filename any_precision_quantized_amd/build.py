@@ -21,8 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libapmoe.so")
 ARCH = os.environ.get("APMOE_ARCH", "gfx950")
 
-HIP_SOURCES = ["route.hip", "permute.hip", "gemv.hip", "gemm.hip", "combine.hip", "pager.hip"]
-CXX_SOURCES = ["planner.cpp"]
+HIP_SOURCES = ["route.hip", "permute.hip", "gemv.hip", "gemm.hip", "combine.hip", "pager.hip", "exp_decode.hip"]
+CXX_SOURCES = ["planner.cpp", "exp_encode.cpp"]
 
 
 def _hipcc() -> str:

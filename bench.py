@@ -190,6 +190,62 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
             "loss": None if during_us is None else round(during_us / idle_us - 1.0, 4)}
 
 
+def codec_probe(inp, reps=5):
+    """Lossless exponent codec on the layer's fp16 weights (the shared expert,
+    else the routed experts at 16 bits): host encode time, coded size, and
+    the GPU decode of all of them timed with events on the current stream."""
+    import numpy as np
+    import torch
+    from any_precision_quantized_amd import _lib
+
+    cfg = inp.cfg
+    mats = []
+    if inp.shared is not None:
+        mats += [inp.shared[m].w16 for m in ("gate", "up", "down")]
+    for e, b in enumerate(inp.bits if inp.bits is not None else []):
+        if int(b) == 16:
+            mats += [inp.experts[e][m].w16 for m in ("gate", "up", "down")]
+    mats = [m for m in mats if m is not None]
+    if not mats:
+        return None
+    t0 = time.perf_counter()
+    encs = [_lib.exp_encode(np.ascontiguousarray(m).view(np.uint16).reshape(-1)) for m in mats]
+    enc_s = time.perf_counter() - t0
+    dev = []
+    for enc in encs:
+        d = {k: torch.from_numpy(np.ascontiguousarray(enc[k]).view(v)).cuda()
+             for k, v in (("words", np.int32), ("block_off", np.int32), ("lo", np.uint8), ("table", np.int16))}
+        d["out"] = torch.empty(enc["n"], dtype=torch.int16, device="cuda")
+        dev.append(d)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for d in dev:
+            _lib.exp_decode(d["words"], d["block_off"], d["lo"], d["table"], d["out"])
+
+    run()
+    torch.cuda.synchronize()
+    for d, m in zip(dev, mats):   # lossless on every matrix
+        ref = torch.from_numpy(np.ascontiguousarray(m).view(np.int16).reshape(-1)).cuda()
+        if not torch.equal(d["out"], ref):
+            raise RuntimeError("exponent codec: decode differs from the weights")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    raw = sum(2 * enc["n"] for enc in encs)
+    coded = sum(4 * enc["words"].size + enc["lo"].size + 4 * enc["block_off"].size + 2 * 4096 for enc in encs)
+    moved = coded + raw                       # read the coded form, write the weights
+    return {"weights": "fp16 " + ("shared expert" if inp.shared is not None else "experts at 16 bits"),
+            "matrices": len(mats), "raw_bytes": raw, "coded_bytes": coded, "ratio": round(coded / raw, 4),
+            "encode_host_s": round(enc_s, 3), "decode_us": round(us, 2),
+            "decode_GBps": round(raw / (us * 1e-6) / 1e9, 1),
+            "decode_hbm_frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +256,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paging-probe", action="store_true",
                     help="skip the throughput-under-plane-paging probe")
+    ap.add_argument("--no-codec-probe", action="store_true",
+                    help="skip the exponent-codec decode probe")
     ap.add_argument("--serial-shared", action="store_true",
                     help="run the shared expert on the main stream instead of the side stream")
     ap.add_argument("--replica-bytes", type=float, default=1.0e9,
@@ -421,6 +479,8 @@ def main():
     if not args.no_paging_probe:
         del tables, shared, steps
         result["paging"] = paging_probe(cfg, inp, bits, mfma_min)
+    if not args.no_codec_probe:
+        result["exp_codec"] = codec_probe(inp)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, bits)
     print(json.dumps(result), flush=True)

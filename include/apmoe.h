@@ -326,6 +326,37 @@ int apmoe_pager_stats(apmoe_pager* pager, uint64_t* resident_bytes, uint64_t* fr
                       uint64_t* largest_free, uint64_t* h2d_bytes, uint64_t* d2d_bytes);
 int apmoe_pager_destroy(apmoe_pager* pager);
 
+/*
+ * Lossless exponent codec for fp16 weights ("专家分页机制：7倍MoE推理吞吐背后的
+ * 显存解耦革命", mubeitech.com, the passage on its third mechanism,
+ * bandwidth-balanced storage tiering: the exponent bits of floating-point
+ * weights are Huffman-coded offline and decoded in GPU memory, in parallel
+ * with host transfers).  Format: a weight's high byte (sign, exponent, top two
+ * mantissa bits) is coded with a canonical Huffman code (ties: key (count,
+ * id), leaves id = symbol, merged nodes 256, 257, ... in creation order),
+ * lengths limited to 12 bits by raising every non-zero count to at least
+ * total >> (12 - r), r = 2, 3, ..., until the code fits; the low byte is kept
+ * raw.  Weights go in groups of 16384: block l (0..63) of group g holds
+ * weights g*16384 + 64j + l, j = 0..min(256, (n - g*16384)/64) - 1; the bit
+ * stream is the blocks' codes in block order, most significant bit first in
+ * 32-bit words, ended by two zero words.
+ *  plan    [host] w: n fp16 bit patterns (n > 0, n % 64 == 0, 12 n < 2^32);
+ *          lengths[256] (out): code length per high byte (0 = absent);
+ *          nwords, nblocks (out): stream words and blocks (64 per group).
+ *  encode  [host] with those lengths: words[nwords] (APMOE_ENOSPACE if
+ *          short), block_off[nblocks] = bit offset of each block, lo[n] = low
+ *          bytes, table[4096] = (length << 8) | symbol for every 12-bit
+ *          prefix.  APMOE_EINVAL for a high byte without a code.
+ *  decode  [device] words, block_off, lo, table as encode wrote them -> out
+ *          fp16 [n], bit-exact.  The stream is read within nwords words
+ *          whatever it holds.
+ */
+int apmoe_exp_plan(const uint16_t* w, uint64_t n, uint8_t* lengths, uint64_t* nwords, uint64_t* nblocks);
+int apmoe_exp_encode(const uint16_t* w, uint64_t n, const uint8_t* lengths, uint32_t* words, uint64_t nwords,
+                     uint32_t* block_off, uint8_t* lo, uint16_t* table);
+int apmoe_exp_decode(const uint32_t* words, uint64_t nwords, const uint32_t* block_off, const uint8_t* lo,
+                     const uint16_t* table, uint64_t n, uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,3 +81,67 @@ def test_round_trip_fp16_weights(n):
         # N(0, 0.02) weights: the high byte carries ~5.5 bits of information
         coded = X.coded_bits(lengths, X.histogram(w >> 8))
         assert coded / n < 6.5
+
+
+# ---------------------------------------------------------------------------
+# The library's host encoder against the oracle (bit-exact)
+# ---------------------------------------------------------------------------
+
+def _native_vs_oracle(w):
+    from any_precision_quantized_amd import _lib
+    got = _lib.exp_encode(w)
+    lengths, words, offs, lo = X.encode(w)
+    assert got["lengths"].tolist() == list(lengths)
+    assert np.array_equal(got["words"], words)
+    assert np.array_equal(got["block_off"], offs)
+    assert np.array_equal(got["lo"], lo)
+    # table entry p: the symbol whose canonical code prefixes the 12 bits p, and its length
+    codes = X.canonical_codes(lengths)
+    want = np.zeros(4096, np.uint16)
+    for s, c in codes.items():
+        L = lengths[s]
+        want[c << (12 - L):(c + 1) << (12 - L)] = (L << 8) | s
+    assert np.array_equal(got["table"], want)
+
+
+@pytest.mark.parametrize("case", ["normal", "partial_group", "one_symbol", "fibonacci"])
+def test_native_encoder_matches_oracle(case):
+    rng = np.random.default_rng(11)
+    if case == "normal":
+        w = rng.normal(0.0, 0.02, 64 * 256 * 2).astype(np.float16).view(np.uint16)
+    elif case == "partial_group":
+        w = rng.normal(0.0, 1.0, 64 * 256 + 64 * 5).astype(np.float16).view(np.uint16)
+    elif case == "one_symbol":
+        w = (np.full(64 * 9, 0x3C00, np.uint16) | rng.integers(0, 256, 64 * 9).astype(np.uint16))
+    else:
+        fib = [1, 1]
+        while len(fib) < 24:
+            fib.append(fib[-1] + fib[-2])
+        hi = np.repeat(np.arange(24), [max(1, f // 200) for f in fib])
+        hi = np.resize(hi, 64 * 300)
+        w = (hi.astype(np.uint16) << 8) | rng.integers(0, 256, hi.size).astype(np.uint16)
+    _native_vs_oracle(w)
+
+
+def test_native_encoder_argument_errors():
+    import ctypes
+    from any_precision_quantized_amd import _lib
+    lib = _lib._lib()
+    w = np.zeros(128, np.uint16)
+    lengths = np.zeros(256, np.uint8)
+    nw, nb = ctypes.c_uint64(), ctypes.c_uint64()
+    assert lib.apmoe_exp_plan(w.ctypes.data, 100, lengths.ctypes.data, ctypes.byref(nw), ctypes.byref(nb)) == _lib.EINVAL
+    assert lib.apmoe_exp_plan(None, 128, lengths.ctypes.data, ctypes.byref(nw), ctypes.byref(nb)) == _lib.EINVAL
+    assert lib.apmoe_exp_plan(w.ctypes.data, 128, lengths.ctypes.data, ctypes.byref(nw), ctypes.byref(nb)) == _lib.OK
+    assert (nw.value, nb.value) == (4 + 2, 64) and lengths[0] == 1   # one symbol: 128 one-bit codes
+    words = np.zeros(nw.value, np.uint32)
+    offs = np.zeros(nb.value, np.uint32)
+    lo = np.zeros(128, np.uint8)
+    table = np.zeros(4096, np.uint16)
+    args = (offs.ctypes.data, lo.ctypes.data, table.ctypes.data)
+    assert lib.apmoe_exp_encode(w.ctypes.data, 128, lengths.ctypes.data, words.ctypes.data, 3, *args) == _lib.ENOSPACE
+    bad = lengths.copy()
+    bad[0] = 0                                   # the only symbol has no code
+    assert lib.apmoe_exp_encode(w.ctypes.data, 128, bad.ctypes.data, words.ctypes.data, nw.value, *args) == _lib.EINVAL
+    assert lib.apmoe_exp_encode(w.ctypes.data, 128, lengths.ctypes.data, words.ctypes.data, nw.value, *args) == _lib.OK
+    assert lib.apmoe_exp_decode(None, 6, None, None, None, 128, None, None) == _lib.EINVAL
