@@ -137,6 +137,11 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     stream = torch.cuda.current_stream()
     low = np.where((bits > 3) & (bits <= 6), bits - 1, bits).astype(np.int8)
 
+    def start():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return [e]
+
     def enqueue(n, evs):
         for _ in range(n):
             lay.forward(x)
@@ -150,8 +155,8 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     for _ in range(10):
         lay.forward(x)
     torch.cuda.synchronize()
-    evs = []
-    enqueue(2 * steps + 1, evs)
+    evs = start()
+    enqueue(2 * steps, evs)
     torch.cuda.synchronize()
     idle = step_us(evs)
     during, copy_ms, h2d, d2d = [], [], 0, 0
@@ -159,8 +164,8 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
         if pe.apply(low) != _lib.OK:
             raise RuntimeError("paging probe: demotion did not fit")
         torch.cuda.synchronize()
-        evs = []
-        enqueue(steps + 1, evs)
+        evs = start()
+        enqueue(steps, evs)
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(pe.copy_stream)
         if pe.stage(bits) != _lib.OK:
