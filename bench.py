@@ -70,17 +70,53 @@ def algorithmic(cfg, bits, counts, mfma_min, n_shared=0):
     return by, flops, fl
 
 
-def cpu_baseline(inp, bits):
-    """The float64 oracle on the host cores, one full step of the same workload."""
+def cpu_baseline(inp, bits, min_s=10.0):
+    """The float64 oracle on the host cores: whole layer steps of the same
+    workload, repeated until about min_s seconds of work (at least one)."""
     from threadpoolctl import threadpool_info
     from oracle import moe
     t0 = time.perf_counter()
     moe.layer(inp, bits=bits)
+    first = time.perf_counter() - t0
+    reps = max(1, int(math.ceil(min_s / max(first, 1e-3))))
+    for _ in range(reps - 1):
+        moe.layer(inp, bits=bits)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": inp.cfg.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full layer step ({inp.cfg.T} tokens) of the same workload in float64 NumPy, "
-                      f"{dt:.1f} s; BLAS threads {threads} of {len(os.sched_getaffinity(0))} host cores"}
+    return {"value": inp.cfg.T * reps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full layer step(s) ({inp.cfg.T} tokens each) of the same workload in float64 "
+                      f"NumPy, {dt:.1f} s; BLAS threads {threads} of {len(os.sched_getaffinity(0))} host cores"}
+
+
+def planner_probe(inp, reps=200):
+    """Host planner calls at this layer's size (the library's C++ planner):
+    one greedy plan, and one online step per KV size while the KV footprint
+    sweeps from nothing to the budget slack and back."""
+    import numpy as np
+    import synth
+    from any_precision_quantized_amd import _lib
+
+    cfg = inp.cfg
+    pl = inp.plan if inp.plan is not None else synth.gen.planner_inputs(cfg, synth.gen.zipf_prior(cfg.E, 1.1))
+    args = (pl["levels"], pl["harm"], pl["bytes"], pl["floors"], pl["budget"])
+    _lib.plan_bitwidths(*args)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        st, bits = _lib.plan_bitwidths(*args)
+    greedy_us = (time.perf_counter() - t0) / reps * 1e6
+    nb = np.asarray(pl["bytes"], dtype=np.uint64)
+    m_total = int(nb[:, 0].sum())
+    slack = m_total - int(nb[:, -1].sum())
+    stage_bits = np.asarray(pl["levels"][1:], dtype=np.int8)
+    kv = [int(slack * (1 - abs(1 - 2 * i / (reps - 1)))) for i in range(reps)]
+    now = np.full(cfg.E, int(pl["levels"][0]), dtype=np.int8)
+    t0 = time.perf_counter()
+    for m_kv in kv:
+        st, now, stage = _lib.plan_online(pl["levels"], pl["harm"], nb, pl["floors"], stage_bits, m_total, m_kv,
+                                          slack // 64, now)
+    online_us = (time.perf_counter() - t0) / reps * 1e6
+    return {"experts": int(cfg.E), "levels": len(pl["levels"]), "plan_bitwidths_us": round(greedy_us, 2),
+            "plan_online_step_us": round(online_us, 2)}
 
 
 def counted_traffic(kernel):
@@ -486,6 +522,7 @@ def main():
         result["paging"] = paging_probe(cfg, inp, bits, mfma_min)
     if not args.no_codec_probe:
         result["exp_codec"] = codec_probe(inp)
+    result["planner"] = planner_probe(inp)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, bits)
     print(json.dumps(result), flush=True)
