@@ -21,18 +21,83 @@ constexpr int kPlanes = 6;
 
 __host__ __device__ inline bool valid_bits(int b) { return (b >= 3 && b <= 6) || b == 16; }
 
-// Wave-wide sum in a fixed order (xor butterfly), so every lane gets the same
-// bit-identical total regardless of scheduling.
+// Cross-lane moves inside a 16-lane row (DPP: VALU operations, no LDS round
+// trip): swap lanes 2i and 2i + 1, swap pairs inside a quad, mirror each
+// half row, mirror the row.  Applied in this order, each step combines a lane
+// with one holding the rest of its group, so after the four steps every lane
+// of a row holds the row's combination; lanes 0, 16, 32 and 48 are then read
+// into scalars and combined in a fixed order.  Every lane gets the same
+// result, independent of scheduling.
+constexpr int kDppQuad1032 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuad2301 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int C>
+__device__ inline uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, C, 0xF, 0xF, true);
+}
+template <int C>
+__device__ inline double dpp64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t r = (uint64_t)dpp32<C>((uint32_t)u) | ((uint64_t)dpp32<C>((uint32_t)(u >> 32)) << 32);
+    return __builtin_bit_cast(double, r);
+}
+template <int C>
+__device__ inline float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp32<C>(__builtin_bit_cast(uint32_t, v)));
+}
+__device__ inline uint32_t lane_u32(uint32_t v, int lane) { return (uint32_t)__builtin_amdgcn_readlane((int)v, lane); }
+__device__ inline double lane_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    return __builtin_bit_cast(double, (uint64_t)lane_u32((uint32_t)u, lane) |
+                                          ((uint64_t)lane_u32((uint32_t)(u >> 32), lane) << 32));
+}
+
+// Wave-wide sums in a fixed order (rows by DPP, then (r0 + r1) + (r2 + r3)).
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_f<kDppQuad1032>(v);
+    v += dpp_f<kDppQuad2301>(v);
+    v += dpp_f<kDppRowHalfMirror>(v);
+    v += dpp_f<kDppRowMirror>(v);
+    const float r0 = __builtin_bit_cast(float, lane_u32(__builtin_bit_cast(uint32_t, v), 0));
+    const float r1 = __builtin_bit_cast(float, lane_u32(__builtin_bit_cast(uint32_t, v), 16));
+    const float r2 = __builtin_bit_cast(float, lane_u32(__builtin_bit_cast(uint32_t, v), 32));
+    const float r3 = __builtin_bit_cast(float, lane_u32(__builtin_bit_cast(uint32_t, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 __device__ inline double wave_sum(double v) {
+    v += dpp64<kDppQuad1032>(v);
+    v += dpp64<kDppQuad2301>(v);
+    v += dpp64<kDppRowHalfMirror>(v);
+    v += dpp64<kDppRowMirror>(v);
+    return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
+}
+
+// Wave-wide argmax over (value, index): the larger value, ties to the lower
+// index (a total order, so the result does not depend on the combining order).
+__device__ inline void take_max(double& v, int& e, double ov, int oe) {
+    if (ov > v || (ov == v && oe < e)) {
+        v = ov;
+        e = oe;
+    }
+}
+template <int C>
+__device__ inline void argmax_step(double& v, int& e) {
+    take_max(v, e, dpp64<C>(v), (int)dpp32<C>((uint32_t)e));
+}
+__device__ inline void wave_argmax(double& v, int& e) {
+    argmax_step<kDppQuad1032>(v, e);
+    argmax_step<kDppQuad2301>(v, e);
+    argmax_step<kDppRowHalfMirror>(v, e);
+    argmax_step<kDppRowMirror>(v, e);
+    double bv = lane_f64(v, 0);
+    int be = (int)lane_u32((uint32_t)e, 0);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    for (int r = 1; r < 4; ++r) take_max(bv, be, lane_f64(v, 16 * r), (int)lane_u32((uint32_t)e, 16 * r));
+    v = bv;
+    e = be;
 }
 
 __device__ inline float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

@@ -8,7 +8,7 @@
 // dimension (four columns each per 256), so one 16-byte router-weight load
 // feeds four tokens and the tile's weights and activations cross the CU once.
 // Products and sums are fp64 (an fp16 x fp32 product is exact in fp64); each
-// lane's partial sums meet in a fixed xor butterfly, so a logit never depends
+// lane's partial sums meet in a fixed reduction order, so a logit never depends
 // on scheduling.  The logits go to the workspace; the select kernel then runs
 // one wave per token: k rounds of a wave-wide argmax (ties to the lower
 // expert), then the softmax over the k chosen logits in fp64.
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* _
 // k rounds of a wave-wide argmax over v (lane's experts lane + 64c), ties to
 // the lower expert, then the softmax over the chosen logits in fp64: lane j
 // takes the exponentials of chosen logits j, j + 64, ... and the wave adds
-// them in a fixed butterfly.  chosen: k doubles of LDS for this wave.
+// them in a fixed order.  chosen: k doubles of LDS for this wave.
 template <int kPer>
 __device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int t, int lane, double* chosen,
                                             int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
@@ -85,12 +85,7 @@ __device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int
             const int e = lane + kWave * c;
             if (e < E && (v[c] > best || (v[c] == best && e < best_e))) { best = v[c]; best_e = e; }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const double ov = __shfl_xor(best, o, kWave);
-            const int oe = __shfl_xor(best_e, o, kWave);
-            if (ov > best || (ov == best && oe < best_e)) { best = ov; best_e = oe; }
-        }
+        wave_argmax(best, best_e);
         // every lane holds the same winner; its owner drops it from the race
 #pragma unroll
         for (int c = 0; c < kPer; ++c)
@@ -209,9 +204,9 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
 
 // Routing statistics (the planner's online inputs).  norms_kernel: one wave
 // per token, ||x_t||_2 with the squares summed in fp32 and met in a fixed
-// butterfly.  stats_kernel: one 16-wave workgroup per expert scans the T*k
+// order.  stats_kernel: one 16-wave workgroup per expert scans the T*k
 // slots (thread i takes slots i, i + 1024, ...) adding its gates and gate *
-// norm in fp32; lanes meet in a fixed butterfly and the 16 waves in index
+// norm in fp32; lanes meet in a fixed order and the 16 waves in index
 // order, so the sums never depend on scheduling.
 __global__ __launch_bounds__(4 * kWave) void norms_kernel(const half_t* __restrict__ x, int T, int H,
                                                           float* __restrict__ norms) {
