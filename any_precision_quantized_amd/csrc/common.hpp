@@ -75,6 +75,19 @@ __device__ inline double wave_sum(double v) {
     return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
 }
 
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside each row by
+// row shifts, then row 0's total into row 1, row 2's into row 3, and rows
+// 0-1's into rows 2-3 by the row broadcasts).
+__device__ inline int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 // Wave-wide argmax over (value, index): the larger value, ties to the lower
 // index (a total order, so the result does not depend on the combining order).
 __device__ inline void take_max(double& v, int& e, double ov, int oe) {

@@ -66,27 +66,22 @@ __device__ __forceinline__ bool find_tile_item(const GemmArgs& a, int RT, int id
         }
         const int nt = (m + kTToks - 1) / kTToks;
         const int n = (m > 0 && m >= a.mfma_min_tokens && valid_bits(b)) ? nt * RT : 0;
-        int inc = n;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int t = __shfl_up(inc, o, kWave);
-            if (lane >= o) inc += t;
-        }
+        const int inc = wave_incl_scan(n);
         const int first = base + inc - n;
         const unsigned long long hit = __ballot(n > 0 && idx >= first && idx < first + n);
         if (hit) {
             const int src = __ffsll((long long)hit) - 1;
             it.e = __builtin_amdgcn_readfirstlane(c0 + src);
-            it.m = __builtin_amdgcn_readfirstlane(__shfl(m, src, kWave));
-            it.b = __builtin_amdgcn_readfirstlane(__shfl(b, src, kWave));
-            const int q = __builtin_amdgcn_readfirstlane(idx - __shfl(first, src, kWave));
+            it.m = __builtin_amdgcn_readlane(m, src);
+            it.b = __builtin_amdgcn_readlane(b, src);
+            const int q = idx - __builtin_amdgcn_readlane(first, src);
             const int ntile = (it.m + kTToks - 1) / kTToks;
             it.rt = q / ntile;
             it.tt = q % ntile;
             it.off = a.offsets[it.e];
             return true;
         }
-        base += __shfl(inc, kWave - 1, kWave);
+        base += __builtin_amdgcn_readlane(inc, kWave - 1);
     }
     return false;
 }

@@ -117,25 +117,20 @@ __device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, in
             b = a.bits[e];
         }
         const int n = (m > 0 && m < a.mfma_min_tokens && valid_bits(b)) ? nrb : 0;
-        int inc = n;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int t = __shfl_up(inc, o, kWave);
-            if (lane >= o) inc += t;
-        }
+        const int inc = wave_incl_scan(n);
         const int first = base + inc - n;
         const unsigned long long hit = __ballot(n > 0 && blk >= first && blk < first + n);
         if (hit) {
             const int src = __ffsll((long long)hit) - 1;
             it.e = __builtin_amdgcn_readfirstlane(c0 + src);
-            it.m = __builtin_amdgcn_readfirstlane(__shfl(m, src, kWave));
-            it.b = __builtin_amdgcn_readfirstlane(__shfl(b, src, kWave));
-            it.rb = __builtin_amdgcn_readfirstlane(blk - __shfl(first, src, kWave));
+            it.m = __builtin_amdgcn_readlane(m, src);
+            it.b = __builtin_amdgcn_readlane(b, src);
+            it.rb = blk - __builtin_amdgcn_readlane(first, src);
             it.off = a.offsets[it.e];
             it.ks = idx % KS;
             return true;
         }
-        base += __shfl(inc, kWave - 1, kWave);
+        base += __builtin_amdgcn_readlane(inc, kWave - 1);
     }
     return false;
 }
