@@ -223,9 +223,15 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
         xrow[j] = (uint32_t)row * (uint32_t)sh.K * 2u;
     }
     char* ring = lds + kXRing;
-    // activations travel global -> registers (two steps ahead) -> LDS ring
-    // slot (one step ahead); xs[k] holds the step with (step - s0) % 2 == k
-    half8_t xs[2][TT];
+    // activations travel global -> registers (XD steps ahead) -> LDS ring
+    // slot (one step ahead); xs[k] holds the step with (step - s0) % NXB == k.
+    // Vector loads retire in order, so waiting for a step's activations also
+    // waits for every load issued before them: on the W32 path they are
+    // loaded as far ahead as the plane words (XD = D), so that wait never
+    // cuts the planes' prefetch distance short.
+    constexpr int XD = W32 ? D : 2;
+    constexpr int NXB = W32 ? NB : 2;
+    half8_t xs[NXB][TT];
     auto x_load = [&](half8_t (&x)[TT], int s) {   // steps past s1 read zeros
         const __amdgpu_buffer_rsrc_t r = make_rsrc(sh.in, s < s1 ? sh.in_bytes : 0u);
         const int col = 128 * s + 8 * xc;
@@ -382,8 +388,8 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
                 }
             }
         };
-        x_load(xs[0], s0);
-        x_load(xs[1], s0 + 1);
+#pragma unroll
+        for (int u = 0; u < XD; ++u) x_load(xs[u], s0 + u);
 #pragma unroll
         for (int u = 0; u < D; ++u) p_load(pw[u], s0 + u);
         x_store(xs[0], 0);
@@ -392,10 +398,10 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
                 const int st = s + u;   // past s1 (the last group's tail): loads read zeros, no MFMAs
-                x_load(xs[u % 2], st + 2);
+                x_load(xs[(u + XD) % NXB], st + XD);
                 p_load(pw[(u + D) % NB], st + D);
                 if (live && st < s1) compute(pw[u], (st - s0) & 1);
-                x_store(xs[(u + 1) % 2], (st + 1 - s0) & 1);
+                x_store(xs[(u + 1) % NXB], (st + 1 - s0) & 1);
                 __syncthreads();
             }
         }
