@@ -159,6 +159,35 @@ __device__ __forceinline__ void stage_luts(char* tab, const Mats& mv, int rowc, 
     }
 }
 
+// 3-bit experts on the 32-row path look up two codes at once: per row and
+// matrix, a table of the 64 code pairs (c0, c1) -> (lut[c0], lut[c1]) as one
+// fp16 pair (the MFMA operand dword of two adjacent columns), gate at 0 and up
+// at 16 KB, entry of pair p for row slot r at p * 256 + 4 * r.  Lane
+// (r = lane % 16, g = lane / 16) of wave w writes the pairs with c0 = 2g,
+// 2g + 1 of row slot 16 w + r.
+constexpr int kPairTable = 64 * 256;
+template <int NMAT>
+__device__ __forceinline__ void stage_pair_luts(char* lds, const Mats& mv, int rowc, int wave, int lane) {
+    const int sl = lane & 15, g = lane >> 4;
+    const int row = rowc + sl;
+#pragma unroll
+    for (int mat = 0; mat < NMAT; ++mat) {
+        const gu32_t* l = mv.lut[mat] + (size_t)row * 4;   // eight halves
+        uint32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = l[j];
+        const uint32_t d = l[g];                           // halves c0 = 2g, 2g + 1
+        char* tab = lds + mat * kPairTable + 64 * wave + 4 * sl + 2 * g * 256;
+#pragma unroll
+        for (int c1 = 0; c1 < 8; ++c1)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t sel = (j ? 0x0302u : 0x0100u) | ((c1 & 1) ? 0x07060000u : 0x05040000u);
+                *reinterpret_cast<uint32_t*>(tab + (j + 8 * c1) * 256) = __builtin_amdgcn_perm(h[c1 >> 1], d, sel);
+            }
+    }
+}
+
 // Results of one 16-token tile in this lane (rows row..row+3, token tok): the
 // final value, or this K split's partial sums.
 template <int NMAT>
@@ -222,7 +251,11 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
         const int row = NMAT == 2 ? sh.slots[it.off + nn] / sh.k : it.off + nn;
         xrow[j] = (uint32_t)row * (uint32_t)sh.K * 2u;
     }
-    char* ring = lds + kXRing;
+    // 3-bit experts on the 32-row path keep pair tables (one per matrix) in
+    // the first 32 KB; the ring follows them
+    constexpr bool kPair = W32 && B == 3;
+    static_assert(!kPair || 2 * kPairTable + 2 * TT * kXTile <= kLdsBytes, "pair tables and ring fit");
+    char* ring = lds + (kPair ? 2 * kPairTable : kXRing);
     // activations travel global -> registers (XD steps ahead) -> LDS ring
     // slot (one step ahead); xs[k] holds the step with (step - s0) % NXB == k.
     // Vector loads retire in order, so waiting for a step's activations also
@@ -344,22 +377,42 @@ __device__ __forceinline__ void kpass(const GemmArgs& a, char* lds, const Shape&
             // Every lookup of the step (four column groups, both matrices) is
             // issued before the first MFMA that needs one, so the step pays one
             // LDS round trip instead of one per column group; a permute packs
-            // each pair of looked-up halves into one operand dword.
+            // each pair of looked-up halves into one operand dword (3-bit
+            // pair tables return the dword whole: byte u of pc[mat][c] is the
+            // pair code of columns 8u + 2c, 8u + 2c + 1).
             {
                 uint32x4_t w[4][NMAT];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t sel = 0x0C0C0400u | ((uint32_t)q << 8);
+                if constexpr (kPair) {
+                    uint32_t pc[NMAT][4];
 #pragma unroll
                     for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const uint32_t lo = *reinterpret_cast<const uint16_t*>(
-                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
-                            const uint32_t hi = *reinterpret_cast<const uint16_t*>(
-                                lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
-                            w[q][mat][c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-                        }
+                        for (int c = 0; c < 4; ++c) pc[mat][c] = qv[mat][2 * c] | (qv[mat][2 * c + 1] << 3);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t sel = 0x0C0C0400u | ((uint32_t)q << 8);
+#pragma unroll
+                        for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                w[q][mat][c] = *reinterpret_cast<const uint32_t*>(
+                                    lds + mat * kPairTable + __builtin_amdgcn_perm(pc[mat][c], lane_off, sel));
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t sel = 0x0C0C0400u | ((uint32_t)q << 8);
+#pragma unroll
+                        for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const uint32_t lo = *reinterpret_cast<const uint16_t*>(
+                                    lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c], lane_off, sel));
+                                const uint32_t hi = *reinterpret_cast<const uint16_t*>(
+                                    lds + 2 * mat + __builtin_amdgcn_perm(qv[mat][2 * c + 1], lane_off, sel));
+                                w[q][mat][c] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                            }
+                    }
                 }
                 if constexpr (W32) {
                     // B operand: token nn, columns 32 (2 hp + h32) + 8q + 0..7
@@ -454,7 +507,12 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, char* lds, const Sha
     const int s0 = min(sh.nsteps, it.ks * per), s1 = min(sh.nsteps, s0 + per);
     if (s0 >= s1) return;   // uniform over the workgroup
     if constexpr (B != 16) {
-        if (live) stage_luts<NMAT, B>(lds + 64 * wave, mv, rowc, lane);
+        if (live) {
+            if (B == 3 && it.m <= 32)
+                stage_pair_luts<NMAT>(lds, mv, rowc, wave, lane);
+            else
+                stage_luts<NMAT, B>(lds + 64 * wave, mv, rowc, lane);
+        }
     }
     if constexpr (B != 16) {
         if (it.m <= 32) {   // one pass of 32-row MFMA blocks
