@@ -52,7 +52,13 @@
 //     different banks whatever the codes;
 //   * a second permute packs each pair of looked-up halves into an operand
 //     dword, and every lookup of a step is issued before its first MFMA.
-// Only the top b planes of a b-bit expert are read.
+//   * 3-bit experts on the 32-row path instead keep, per row and matrix, a
+//     table of the 64 code pairs (one fp16 pair = one operand dword), so one
+//     32-bit lookup replaces two 16-bit lookups and the packing permute.
+// Only the top b planes of a b-bit expert are read.  On the 32-row path the
+// activations are loaded as far ahead as the plane words: vector loads retire
+// in order, so a nearer activation load would make its wait also wait for
+// the planes issued before it.
 //
 // When the host splits K (only when the items of the possible experts would
 // leave CUs idle), each split writes fp32 partial sums to the workspace and a
