@@ -255,6 +255,28 @@ class MoELayer:
         _lib.combine(self.Y, self.pos_of_slot, self.topk_w, T, k, H, ysh, self.out, n)
         return self.out
 
+    def graph(self, x, experts: Optional[ExpertTable] = None, shared: Optional[ExpertTable] = None):
+        """One forward step captured as a HIP graph: g.replay() reruns the
+        whole layer on x with these weights (router, grouping, both expert
+        stages, combine) and leaves the result in the buffer forward()
+        returns.  The step enqueues kernels only (no copies, fills or
+        allocations); an eager warm-up call first builds the descriptor table
+        of the fused shared expert.  A shared expert that runs on the second
+        stream (its size no multiple of the routed one) is not captured."""
+        import torch
+        sh = self.shared if shared is None else shared
+        if sh is not None and not self.n_shared:
+            raise ValueError("graph(): only a layer whose shared expert runs as always-on experts can be captured")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.forward(x, experts, shared)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, experts, shared)
+        return g
+
 
 def harm_multipliers(mass, wnorm):
     """Per-expert multipliers of the offline harm table from one step's routing

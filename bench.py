@@ -119,10 +119,10 @@ def planner_probe(inp, reps=200):
             "plan_online_step_us": round(online_us, 2)}
 
 
-def counted_traffic(kernel):
-    """HBM bytes per launch of `kernel` from a committed counter summary under
-    profiles/, or None when there is none or the kernel's sources changed since
-    the counters were taken."""
+def counted_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from a committed counter
+    summary under profiles/, or None when there is none for that kernel and
+    workload or the kernel's sources changed since the counters were taken."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -130,10 +130,12 @@ def counted_traffic(kernel):
         with open(path) as f:
             for line in f:
                 line = line.strip()
-                for key in ("traffic_kernel", "traffic_bytes_per_launch", "sources", "sources_sha256"):
+                for key in ("traffic_kernel", "traffic_workload", "traffic_bytes_per_launch", "sources",
+                            "sources_sha256"):
                     if line.startswith(key + ":"):
                         fields[key] = line.split(":", 1)[1].strip()
-        if fields.get("traffic_kernel") != kernel or "sources" not in fields:
+        if fields.get("traffic_kernel") != kernel or fields.get("traffic_workload") != workload \
+                or "sources" not in fields:
             continue
         h = hashlib.sha256()
         try:
@@ -299,6 +301,8 @@ def main():
                     help="skip the throughput-under-plane-paging probe")
     ap.add_argument("--no-codec-probe", action="store_true",
                     help="skip the exponent-codec decode probe")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no HIP graph replay of the step)")
     ap.add_argument("--serial-shared", action="store_true",
                     help="run the shared expert on the main stream instead of the side stream")
     ap.add_argument("--replica-bytes", type=float, default=1.0e9,
@@ -473,6 +477,21 @@ def main():
     dt = time.perf_counter() - t0
     dom_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
 
+    ms_eager = dt / args.steps * 1e3
+    # The same K steps replayed as HIP graphs (one per weight replica): what a
+    # serving loop that captures the layer pays, without per-launch host work.
+    use_graph = not args.no_graph and side is None
+    if use_graph:
+        graphs = [layer.graph(x, tables[r], shared[r]) for r in range(R)]
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del graphs
     ms_per_step = dt / args.steps * 1e3
     tokens_per_s = T * args.steps / dt
     layer_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -483,12 +502,12 @@ def main():
         roofline = {"bound": "mfma", "kernel": dominant, "achieved": dom_flops / (dom_us * 1e-6) / 1e12,
                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": dom_flops / (dom_us * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
-                    "traffic": counted_traffic(dominant), "algorithmic_flops": dom_flops,
+                    "traffic": counted_traffic(dominant, cfg.name), "algorithmic_flops": dom_flops,
                     "algorithmic_bytes": dom_bytes, "avg_us": dom_us}
     else:
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(dominant),
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(dominant, cfg.name),
                     "algorithmic_bytes": dom_bytes, "avg_us": dom_us}
     result = {
         "metric": METRIC,
@@ -506,9 +525,10 @@ def main():
         "config": {"workload": f"{cfg.name}: E{E} H{H} I{I} top-{k} T{T}"
                                + (f" + fp16 shared expert I{cfg.shared_I}" if cfg.shared_I else "")
                                + f", bits {dict(sorted((int(b), int((bits == b).sum())) for b in set(bits.tolist())))}",
-                   "mfma_min_tokens": mfma_min, "weight_replicas": R,
+                   "mfma_min_tokens": mfma_min, "weight_replicas": R, "hip_graph": use_graph,
                    "shared_as_always_on_experts": nsh,
                    "groups": sorted([int(c) for c in counts[nsh:] if c > 0], reverse=True)},
+        "ms_per_step_eager": ms_eager,
         "hbm_gbs": layer_gbs,
         "hbm_frac": layer_gbs / HBM_PEAK_GBS,
         "expert_tflops": flops / (ms_per_step * 1e-3) / 1e12,
