@@ -41,6 +41,14 @@ SMALL = {
     "fp16_wide": synth.custom("fp16_wide", E=2, H=128, I=192, k=2, T=70, bits=(16, 16)),
     # shared expert whose size is no multiple of I: its own launches on a side stream
     "shared_side": synth.custom("shared_side", E=4, H=160, I=128, k=1, T=33, bits=(6, 3, 4, 5), shared_I=224),
+    # the largest expert count (256): router lanes hold four experts, the item
+    # lookups scan four chunks of 64 experts
+    "max_experts": synth.custom("max_experts", E=256, H=64, I=96, k=8, T=48,
+                                bits=tuple((3, 4, 5, 6, 16)[e % 5] for e in range(256))),
+    # 252 routed experts + a shared expert of 4x the routed size as 4 always-on
+    # experts: 256 experts in the grouping and the expert launches
+    "max_experts_shared": synth.custom("max_experts_shared", E=252, H=64, I=64, k=4, T=40,
+                                       bits=tuple((6, 5, 4, 3)[e % 4] for e in range(252)), shared_I=256),
 }
 
 
