@@ -60,10 +60,11 @@
 // in order, so a nearer activation load would make its wait also wait for
 // the planes issued before it.
 //
-// When the host splits K (only when the items of the possible experts would
-// leave CUs idle), each split writes fp32 partial sums to the workspace and a
-// finalize kernel adds them in split order (and applies SwiGLU), so results
-// never depend on scheduling.
+// When the host splits K (only while each split keeps enough K steps to repay
+// an item's prologue and the launch stays within about four workgroups per
+// CU), each split writes fp32 partial sums to the workspace and a finalize
+// kernel adds them in split order (and applies SwiGLU), so results never
+// depend on scheduling.
 #include <algorithm>
 
 #include "common.hpp"
@@ -84,7 +85,7 @@ constexpr int kLutBytes = 64 * 256;
 constexpr int kXRing = kLutBytes;
 constexpr int kLdsBytes = kXRing + 2 * kMaxTiles * kXTile;
 static_assert(kLdsBytes <= 48 * 1024, "three workgroups per CU");
-constexpr int kTargetGroups = 1024;          // 256 CUs x 2 resident workgroups, twice over
+constexpr int kTargetGroups = 1024;          // workgroups a K split may grow a launch to (4 per CU)
 
 // Weight sources of one item.  Buffer resources are rebuilt per load group
 // with num_records = 0 when the group is not needed, so every load is issued
@@ -655,14 +656,19 @@ long long items_per_split(int T, int k, int E, int rows) {
 
 }  // namespace
 
-// K splits, chosen from shapes alone: only when one item per 64-row block of
-// every expert that could be active would leave CUs idle (at least 4 K steps
-// per split).
+// K splits, chosen from shapes alone: as many as keep the workgroups of every
+// expert that could be active within kTargetGroups, but at least kMinSplitSteps
+// K steps per split, since each split pays an item's prologue (LUT staging and
+// the first steps' loads, about five steps' worth) again.  Measured on the
+// Mixtral-shaped decode layer: one token's gate/up (448 items, 32 steps) is
+// fastest unsplit, its down (128 items, 112 steps) with four splits, and the
+// down stage of 8 or 32 tokens (512 items) with two.
+constexpr int kMinSplitSteps = 28;
 int gemv_splits(int T, int k, int E, int rows, int K) {
     const long long items = items_per_split(T, k, E, rows);
     const int nsteps = (K / 32 + 3) / 4;
-    long long ks = items > 0 ? (kTargetGroups + items - 1) / items : 1;
-    const int cap = nsteps / 4 > 1 ? nsteps / 4 : 1;
+    long long ks = items > 0 ? kTargetGroups / items : 1;
+    const int cap = nsteps / kMinSplitSteps;
     if (ks > cap) ks = cap;
     return ks < 1 ? 1 : (int)ks;
 }

@@ -222,8 +222,9 @@ GRAPH_CASES = {
     "tiny": SMALL["tiny"],                  # one-kernel router
     "shared_fused": SMALL["shared_fused"],  # always-on fp16 experts: tile path at mfma_min 16
     "ragged": SMALL["ragged"],
-    # two experts, one token, K = 1024: the GEMV splits K and runs its finalize kernel
-    "ksplit": synth.custom("ksplit", E=2, H=1024, I=128, k=1, T=1, bits=(5, 3)),
+    # one token over two experts, down stage K = 7168 (56 steps): the down GEMV
+    # splits K in two and runs its finalize kernel
+    "ksplit": synth.custom("ksplit", E=2, H=128, I=7168, k=1, T=1, bits=(5, 3)),
 }
 
 
