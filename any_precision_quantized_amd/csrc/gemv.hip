@@ -112,9 +112,17 @@ struct Item {
 // Item of workgroup `idx`: experts on this path each own ceil(rows / 64) row
 // blocks times KS splits, in expert order.  Every wave finds it on its own
 // (a wave-wide scan over the slot counts); returns false past the last item.
-__device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, int idx, Item& it) {
+//
+// With one K split, at most 64 experts and between 2 and 3 items per CU, ncu
+// is the CU count: the dispatcher places workgroups b, b + ncu and b + 2 ncu
+// on one CU, so the first N - 2 ncu block numbers land on the CUs that hold
+// three items.  The items are then rotated so that those blocks take the last
+// items (the least routed experts, the cheapest) and the head of the expert
+// order (fp16 always-on experts, the most routed ones) lands on CUs that hold
+// two.  With at most 64 experts one wave-wide scan gives both the total and
+// the item, so the rotation costs no extra load.
+__device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, int idx, int ncu, Item& it) {
     const int lane = threadIdx.x % kWave;
-    const int blk = idx / KS;
     int base = 0;
     for (int c0 = 0; c0 < a.E; c0 += kWave) {
         const int e = c0 + lane;
@@ -125,6 +133,13 @@ __device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, in
         }
         const int n = (m > 0 && m < a.mfma_min_tokens && valid_bits(b)) ? nrb : 0;
         const int inc = wave_incl_scan(n);
+        if (c0 == 0 && KS == 1 && a.E <= kWave) {
+            const int total = __builtin_amdgcn_readlane(inc, kWave - 1);
+            if (idx >= total) return false;
+            const int three = total - 2 * ncu;   // CUs that hold a third item
+            if (three > 0 && three <= ncu) idx = (idx - three + total) % total;
+        }
+        const int blk = idx / KS;
         const int first = base + inc - n;
         const unsigned long long hit = __ballot(n > 0 && blk >= first && blk < first + n);
         if (hit) {
@@ -544,7 +559,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, char* lds, const Sha
 
 template <int NMAT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
-void gemv_kernel(GemmArgs a, int KS, float* partial) {
+void gemv_kernel(GemmArgs a, int KS, float* partial, int ncu) {
     __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
 
     Shape sh;
@@ -561,7 +576,7 @@ void gemv_kernel(GemmArgs a, int KS, float* partial) {
     sh.in_bytes = (uint32_t)((NMAT == 2 ? (size_t)a.T : (size_t)sh.S) * sh.K * 2);
 
     Item it;
-    if (!find_item(a, (sh.rows + kItemRows - 1) / kItemRows, KS, blockIdx.x, it)) return;   // uniform
+    if (!find_item(a, (sh.rows + kItemRows - 1) / kItemRows, KS, blockIdx.x, ncu, it)) return;   // uniform
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
@@ -693,10 +708,13 @@ int launch_gemv(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
     const long long groups = items_per_split(a.T, a.k, a.E, rows) * KS;
     if (groups <= 0) return APMOE_OK;
     dim3 grid((unsigned)groups), block(kThreads);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return APMOE_EHIP;
     if (gu)
-        hipLaunchKernelGGL(gemv_kernel<2>, grid, block, 0, s, a, KS, partial);
+        hipLaunchKernelGGL(gemv_kernel<2>, grid, block, 0, s, a, KS, partial, ncu);
     else
-        hipLaunchKernelGGL(gemv_kernel<1>, grid, block, 0, s, a, KS, partial);
+        hipLaunchKernelGGL(gemv_kernel<1>, grid, block, 0, s, a, KS, partial, ncu);
     int rc = launch_status();
     if (rc != APMOE_OK || KS == 1) return rc;
     const long long S = (long long)a.T * a.k;
