@@ -41,6 +41,12 @@ SMALL = {
     "fp16_wide": synth.custom("fp16_wide", E=2, H=128, I=192, k=2, T=70, bits=(16, 16)),
     # shared expert whose size is no multiple of I: its own launches on a side stream
     "shared_side": synth.custom("shared_side", E=4, H=160, I=128, k=1, T=33, bits=(6, 3, 4, 5), shared_I=224),
+    # groups of 33..64 tokens on 3-, 6- and 4-bit experts (the 64-token GEMV
+    # pass), rows not a multiple of 64
+    "mid_groups": synth.custom("mid_groups", E=3, H=224, I=352, k=2, T=60, bits=(3, 6, 4)),
+    # the same with a long down projection (K = 7168, 56 steps): 64-token
+    # passes under a K split
+    "mid_groups_ksplit": synth.custom("mid_groups_ksplit", E=2, H=128, I=7168, k=1, T=90, bits=(3, 5)),
     # the largest expert count (256): router lanes hold four experts, the item
     # lookups scan four chunks of 64 experts
     "max_experts": synth.custom("max_experts", E=256, H=64, I=96, k=8, T=48,
