@@ -1,7 +1,7 @@
 // Router: top-k over the router logits, then a softmax over the k chosen.
 //
 // A few tokens over a small router matrix run one kernel (route_kernel): a
-// workgroup takes one or two tokens, computes their logits for every expert
+// workgroup takes one token, computes its logits for every expert
 // into LDS and selects from there, so no logit leaves the CU and the layer
 // pays one launch.  Everything else runs two kernels.  The logits kernel tiles (4 tokens x 8 experts) per workgroup:
 // wave w owns experts 2w, 2w+1 of the tile and its lanes split the hidden
@@ -276,12 +276,15 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(const int32_t* __re
 // The fused kernel pays off for a few tokens and a small router matrix:
 // every fused workgroup streams the whole matrix through its CU, and each
 // (token, expert) sum costs four wave reductions, so with more tokens the
-// reductions dominate.  It runs for T <= 32 (one or two tokens per workgroup)
-// when the matrix is at most 160 KB; otherwise the two-kernel path, whose
-// workgroups split the experts, runs.
+// reductions dominate.  It runs for T <= 32 when the matrix is at most
+// 160 KB; otherwise the two-kernel path, whose workgroups split the experts,
+// runs.  One token per workgroup: at 32 tokens over a 128 KB matrix, 32
+// workgroups of one token route in 11.3 us where 16 of two took 15.2 us; at
+// 64 tokens over a 480 KB matrix the fused kernel (16.2 us) no longer beats
+// the two kernels (15 us).
 int fused_tokens(int T, int E, int H) {
     if (T > 32) return 0;
-    const int tb = T > 16 ? 2 : 1;
+    const int tb = 1;
     const double wbytes = (double)E * H * 4.0;
     const double lds = (4.0 * tb * E + (double)kFWaves * E) * sizeof(double);
     return (wbytes <= 160.0 * 1024 && lds <= 65536.0) ? tb : 0;
@@ -313,7 +316,6 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
                            E, k, topk_ids, topk_w);                                                           \
         return launch_status();
         APMOE_ROUTE_FUSED(1)
-        APMOE_ROUTE_FUSED(2)
 #undef APMOE_ROUTE_FUSED
         default: break;
     }
