@@ -3,10 +3,15 @@
 // A few tokens over a small router matrix run one kernel (route_kernel): a
 // workgroup takes one token, computes its logits for every expert
 // into LDS and selects from there, so no logit leaves the CU and the layer
-// pays one launch.  Everything else runs two kernels.  The logits kernel tiles (4 tokens x 8 experts) per workgroup:
-// wave w owns experts 2w, 2w+1 of the tile and its lanes split the hidden
-// dimension (four columns each per 256), so one 16-byte router-weight load
-// feeds four tokens and the tile's weights and activations cross the CU once.
+// pays one launch.  Everything else runs two kernels.  The logits kernel tiles
+// (TB tokens x 8 experts) per workgroup: wave w owns experts 2w, 2w+1 of the
+// tile and its lanes split the hidden dimension (four columns each per 256),
+// so one 16-byte router-weight load feeds TB tokens and the tile's weights and
+// activations cross the CU once.  TB is 4 unless that leaves fewer than two
+// workgroups per CU; then 2, or 1 (router load latency is hidden by more
+// workgroups, not by longer tiles: at 64 tokens x 60 experts, 512 one-token
+// tiles route in 12.2 us against 15.1 us for 128 four-token tiles; at 256
+// tokens x 128 experts four-token tiles are the fastest).
 // Products and sums are fp64 (an fp16 x fp32 product is exact in fp64); each
 // lane's partial sums meet in a fixed reduction order, so a logit never depends
 // on scheduling.  The logits go to the workspace; the select kernel then runs
@@ -17,13 +22,13 @@
 namespace apmoe {
 namespace {
 
-constexpr int kTB = 4;                  // tokens per logits tile
 constexpr int kEPW = 2;                 // experts per wave
 constexpr int kRWaves = 4;
 constexpr int kEB = kEPW * kRWaves;     // experts per logits tile
 
 typedef float float4v_t __attribute__((ext_vector_type(4)));
 
+template <int kTB>
 __global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* __restrict__ x, int T, int H,
                                                                   const float* __restrict__ w_router,
                                                                   const float* __restrict__ bias, float scale,
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __
     }
 }
 
-constexpr int kSelWaves = 4;
+constexpr int kSelWaves = 1;   // one-wave workgroups spread the tokens over the most CUs
 
 __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double* __restrict__ L, int T, int E, int k,
                                                                     int32_t* __restrict__ topk_ids,
@@ -321,9 +326,22 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
     }
     if (!ws || ws_bytes < route_workspace_bytes(T, E, H)) return APMOE_ENOSPACE;
     double* L = reinterpret_cast<double*>(ws);
-    dim3 grid((T + kTB - 1) / kTB, (E + kEB - 1) / kEB);
-    hipLaunchKernelGGL(logits_kernel, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale, E,
-                       L);
+    const int etiles = (E + kEB - 1) / kEB;
+    int ncu = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return APMOE_EHIP;
+    auto tiles = [&](int tb) { return (long long)((T + tb - 1) / tb) * etiles; };
+    const int tb = tiles(4) >= 2LL * ncu ? 4 : tiles(2) >= 2LL * ncu ? 2 : 1;
+    const dim3 grid((T + tb - 1) / tb, etiles);
+    if (tb == 4)
+        hipLaunchKernelGGL(logits_kernel<4>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
+                           E, L);
+    else if (tb == 2)
+        hipLaunchKernelGGL(logits_kernel<2>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
+                           E, L);
+    else
+        hipLaunchKernelGGL(logits_kernel<1>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
+                           E, L);
     int rc = launch_status();
     if (rc != APMOE_OK) return rc;
     hipLaunchKernelGGL(select_kernel, dim3((T + kSelWaves - 1) / kSelWaves), dim3(kSelWaves * kWave), 0, s, L, T, E,
