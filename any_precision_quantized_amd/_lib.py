@@ -53,6 +53,8 @@ def _lib():
             "apmoe_plan_bitwidths": [_c_int, _c_int, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp],
             "apmoe_plan_online": [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, ctypes.c_uint64,
                                   ctypes.c_uint64, ctypes.c_uint64, _vp, _vp, _vp],
+            "apmoe_harm_multipliers": [_c_int, _vp, _vp, _vp],
+            "apmoe_plan_routed": [_c_int, _c_int, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _vp, _vp],
             "apmoe_commit_bits": [_vp, _c_int, _vp, _vp],
             "apmoe_workspace_bytes": [_c_int, _c_int, _c_int, _c_int, _c_int],
             "apmoe_packed_plane_words": [_c_int, _c_int],
@@ -247,6 +249,41 @@ def plan_bitwidths(levels, harm, nbytes, floor_bits, budget):
     out = np.zeros(E, dtype=np.int8)
     rc = _lib().apmoe_plan_bitwidths(E, L, lv.ctypes.data, hm.ctypes.data, nb.ctypes.data,
                                      fl.ctypes.data, int(budget), out.ctypes.data)
+    return rc, out
+
+
+def harm_multipliers(mass, wnorm):
+    """Per-expert harm multipliers from routing statistics (host arrays or
+    sequences of E floats).  Returns float64 [E]."""
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(mass, dtype=np.float32))
+    n = np.ascontiguousarray(np.asarray(wnorm, dtype=np.float32))
+    if m.shape != n.shape or m.ndim != 1:
+        raise ValueError("mass and wnorm must be two [E] arrays")
+    out = np.zeros(m.size, dtype=np.float64)
+    _check(_lib().apmoe_harm_multipliers(m.size, m.ctypes.data, n.ctypes.data, out.ctypes.data),
+           "apmoe_harm_multipliers")
+    return out
+
+
+def plan_routed(levels, harm, nbytes, floor_bits, budget, mass, wnorm):
+    """Greedy plan over harm scaled by the routing multipliers.  Returns
+    (status, bits int8[E]); raises only on EINVAL/EBITS."""
+    import numpy as np
+    lv = np.ascontiguousarray(np.asarray(levels, dtype=np.int8))
+    hm = np.ascontiguousarray(np.asarray(harm, dtype=np.float64))
+    nb = np.ascontiguousarray(np.asarray(nbytes, dtype=np.uint64))
+    fl = np.ascontiguousarray(np.asarray(floor_bits, dtype=np.int8))
+    m = np.ascontiguousarray(np.asarray(mass, dtype=np.float32))
+    n = np.ascontiguousarray(np.asarray(wnorm, dtype=np.float32))
+    E, L = hm.shape
+    if nb.shape != (E, L) or lv.shape != (L,) or fl.shape != (E,) or m.shape != (E,) or n.shape != (E,):
+        raise ValueError("planner input shapes disagree")
+    out = np.zeros(E, dtype=np.int8)
+    rc = _lib().apmoe_plan_routed(E, L, lv.ctypes.data, hm.ctypes.data, nb.ctypes.data, fl.ctypes.data,
+                                  int(budget), m.ctypes.data, n.ctypes.data, out.ctypes.data)
+    if rc not in (OK, ENOSPACE):
+        _check(rc, "apmoe_plan_routed")
     return rc, out
 
 

@@ -17,6 +17,9 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t uint32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+// Largest activation buffer or weight matrix the expert kernels accept: they
+// address it with 32-bit byte offsets from raw buffer resources.
+constexpr long long kMaxBufferBytes = 1ll << 31;
 constexpr int kPlanes = 6;
 
 __host__ __device__ inline bool valid_bits(int b) { return (b >= 3 && b <= 6) || b == 16; }

@@ -369,6 +369,11 @@ extern "C" int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, c
     if (T < 0 || E < 1 || E > APMOE_MAX_EXPERTS || k < 1 || H <= 0 || I <= 0) return APMOE_EINVAL;
     if (H % 32 || I % 32 || mfma_min_tokens < 1) return APMOE_EINVAL;
     if ((long long)T * k > (1ll << 30)) return APMOE_EINVAL;
+    // The kernels address the activation buffer and each weight matrix with
+    // 32-bit byte offsets from raw buffer resources: both must stay below
+    // 2 GiB (the fp16 copy, H * I * 2 bytes, is the largest form of a matrix).
+    const long long in_bytes = stage == APMOE_GATE_UP_SWIGLU ? (long long)T * H * 2 : (long long)T * k * I * 2;
+    if (in_bytes >= kMaxBufferBytes || (long long)H * I * 2 >= kMaxBufferBytes) return APMOE_EINVAL;
     if (T == 0) return APMOE_OK;
     if (!experts || !bits || !offsets || !in || !out) return APMOE_EINVAL;
     if (stage == APMOE_GATE_UP_SWIGLU && !sorted_slots) return APMOE_EINVAL;

@@ -134,3 +134,47 @@ extern "C" int apmoe_plan_online(int E, int L, const int8_t* levels, const doubl
     *stage_out = n_stages - 1;
     return APMOE_ENOSPACE;
 }
+
+// Harm multipliers from one router call's routing statistics.  The planner
+// page ("内存的饥饿游戏", zhichai.net, section "三层感知：离线 + 路由 + 提示词")
+// protects experts that receive more routing and corrects the offline
+// sensitivity table with a residual from routing-weighted input norms; it
+// gives no formula.  Read plainly: load = mass / mean(mass), residual = the
+// mean input norm of the expert's slots against the mean over all slots (1 for
+// an expert with no routing mass), multiplier = load * residual; 1 everywhere
+// when nothing was routed.  Sums run in index order in double precision.
+extern "C" int apmoe_harm_multipliers(int E, const float* mass, const float* wnorm, double* mult) {
+    if (E < 1 || E > APMOE_MAX_EXPERTS || !mass || !wnorm || !mult) return APMOE_EINVAL;
+    double tot_m = 0.0, tot_n = 0.0;
+    for (int e = 0; e < E; ++e) {
+        if (!(mass[e] >= 0.0f) || !(wnorm[e] >= 0.0f)) return APMOE_EINVAL;   // also rejects NaN
+        tot_m += (double)mass[e];
+        tot_n += (double)wnorm[e];
+    }
+    if (!(tot_m > 0.0 && tot_n > 0.0)) {
+        for (int e = 0; e < E; ++e) mult[e] = 1.0;
+        return APMOE_OK;
+    }
+    const double mean_m = tot_m / E, mean_norm = tot_n / tot_m;
+    for (int e = 0; e < E; ++e) {
+        const double m = (double)mass[e];
+        const double load = m / mean_m;
+        const double resid = m > 0.0 ? ((double)wnorm[e] / m) / mean_norm : 1.0;
+        mult[e] = load * resid;
+    }
+    return APMOE_OK;
+}
+
+// The greedy plan over the offline harm table scaled per expert by the
+// routing multipliers: harm'[e][l] = harm[e][l] * mult[e].
+extern "C" int apmoe_plan_routed(int E, int L, const int8_t* levels, const double* harm, const uint64_t* bytes,
+                                 const int8_t* floor_bits, uint64_t budget, const float* mass, const float* wnorm,
+                                 int8_t* bits_out) {
+    if (E < 1 || E > APMOE_MAX_EXPERTS || L < 1 || L > 5 || !harm) return APMOE_EINVAL;
+    std::vector<double> mult(E), scaled((size_t)E * L);
+    const int rc = apmoe_harm_multipliers(E, mass, wnorm, mult.data());
+    if (rc != APMOE_OK) return rc;
+    for (int e = 0; e < E; ++e)
+        for (int l = 0; l < L; ++l) scaled[(size_t)e * L + l] = harm[(size_t)e * L + l] * mult[e];
+    return apmoe_plan_bitwidths(E, L, levels, scaled.data(), bytes, floor_bits, budget, bits_out);
+}

@@ -146,6 +146,9 @@ class MoELayer:
         self.experts = experts
         self.shared = shared
         self.shared_I = shared_I
+        # set by PagedExperts.attach: plans then go through the pager, which
+        # makes the new planes and LUTs resident before the bits take effect
+        self.pager = None
         # always-on experts: the shared expert split into n of the routed size
         self.n_shared = shared_I // I if (shared is not None and shared_I % I == 0) else 0
         n = self.n_shared
@@ -197,8 +200,16 @@ class MoELayer:
         return self._tables[key][0]
 
     def commit(self, bits):
-        """Routed bitwidths (the always-on parts stay at 16)."""
+        """Commit routed bitwidths in stream order (the always-on parts stay at
+        16).  On paged weights the pager stages the planes and LUTs the new
+        bitwidths need and commits them together with the bits; writing the
+        bits table alone would point the kernels at planes that are not
+        resident.  Returns OK, or ENOSPACE when the pager's arena cannot hold
+        the plan (nothing changed)."""
+        if self.pager is not None:
+            return self.pager.apply(bits)
         _lib.commit_bits(bits, self.bits[self.n_shared:])
+        return _lib.OK
 
     def route_stats(self, x):
         """Routing mass and routing-weighted input norm of every routed expert
@@ -209,15 +220,14 @@ class MoELayer:
 
     def replan(self, x, levels, harm, nbytes, floor_bits, budget):
         """Re-plan the routed experts' bitwidths from the offline harm table
-        scaled by this step's routing statistics (see harm_multipliers), commit
+        corrected by this step's routing statistics (apmoe_plan_routed), commit
         the plan in stream order and return (status, bits).  Synchronises to
         read the statistics back."""
         mass, wnorm = self.route_stats(x)
-        h = harm_multipliers(mass.cpu().numpy(), wnorm.cpu().numpy())[0]
-        status, bits = _lib.plan_bitwidths(levels, np.asarray(harm, dtype=np.float64) * h[:, None], nbytes,
-                                           floor_bits, budget)
+        status, bits = _lib.plan_routed(levels, harm, nbytes, floor_bits, budget, mass.cpu().numpy(),
+                                        wnorm.cpu().numpy())
         if status == _lib.OK:
-            self.commit(bits)
+            status = self.commit(bits)
         return status, bits
 
     def forward(self, x, experts: Optional[ExpertTable] = None, shared: Optional[ExpertTable] = None):
@@ -278,40 +288,14 @@ class MoELayer:
         return g
 
 
-def harm_multipliers(mass, wnorm):
-    """Per-expert multipliers of the offline harm table from one step's routing
-    statistics (host, float64).  The planner page ("内存的饥饿游戏…", zhichai.net,
-    section "三层感知：离线 + 路由 + 提示词") protects experts that receive more
-    routing and corrects the offline table with a residual taken from
-    routing-weighted input norms; it gives no formula.  Read plainly:
-        load[e]  = mass[e] / mean_e(mass)             (1 = an average share)
-        resid[e] = (wnorm[e] / mass[e]) / (sum wnorm / sum mass)
-                   (the mean input norm of e's tokens against the mean over all
-                   routed slots; 1 for an expert with no slots)
-        mult[e]  = load[e] * resid[e]
-    so an expert nobody routes to costs nothing to demote.  Returns
-    (mult, load, resid)."""
-    mass = np.asarray(mass, dtype=np.float64)
-    wnorm = np.asarray(wnorm, dtype=np.float64)
-    E = mass.size
-    tot_m, tot_n = float(mass.sum()), float(wnorm.sum())
-    if not (tot_m > 0 and tot_n > 0):
-        one = np.ones(E)
-        return one, one.copy(), one.copy()
-    load = mass / (tot_m / E)
-    routed = mass > 0
-    resid = np.ones(E)
-    resid[routed] = (wnorm[routed] / mass[routed]) / (tot_n / tot_m)
-    return load * resid, load, resid
-
-
 class OnlinePlanner:
     """The layer's bitwidth plan kept up to date as the KV cache grows and
     shrinks: each step recomputes the weight budget M_w = m_total - m_kv and
     runs the staged, floored, hysteretic planner step (apmoe_plan_online); a
     changed plan is committed to the layer in stream order, so the next
     forward call uses it.  `harm` may be replaced per step (for example by the
-    offline table scaled with harm_multipliers of the last routing)."""
+    offline table scaled with the library's harm multipliers of the last
+    routing, _lib.harm_multipliers)."""
 
     def __init__(self, layer, levels, harm, nbytes, floor_bits, stage_bits, m_total, hysteresis, bits_now):
         self.layer = layer
@@ -333,7 +317,9 @@ class OnlinePlanner:
                                                self.stage_bits, self.m_total, m_kv, self.hysteresis, self.bits)
         changed = bits.tolist() != self.bits.tolist()
         if changed:
-            self.layer.commit(bits)
+            rc = self.layer.commit(bits)
+            if rc != _lib.OK:     # the pager could not make the plan resident: keep the old one
+                return rc, self.bits.copy(), -1, False
             self.bits = bits
         if stage >= 0:
             self.stage = stage

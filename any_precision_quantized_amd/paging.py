@@ -81,6 +81,7 @@ class PagedExperts:
         rc = self.apply(bits)
         if rc != _lib.OK:
             raise _lib.ApmoeError(rc, "initial residency")
+        layer.pager = self    # later plans (commit, replan, OnlinePlanner) go through apply
 
     def _check16(self, bits):
         for e, b in enumerate(bits):

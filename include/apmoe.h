@@ -15,10 +15,16 @@
  *  - Returns 0 (APMOE_OK) or a negative APMOE_E* code; apmoe_strerror names it.
  *    Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is launched and no output is touched.
- *  - The caller owns every buffer.  The library never allocates, frees or
- *    synchronises; all GPU work is enqueued on `stream` (a hipStream_t; NULL
- *    means the default stream) in call order.  No global mutable state: calls
- *    on different streams may run concurrently if their buffers are disjoint.
+ *  - The layer entry points (apmoe_route, apmoe_route_stats, apmoe_permute,
+ *    apmoe_bitplane_lut_gemm, apmoe_combine, apmoe_commit_bits,
+ *    apmoe_pack_planes, apmoe_exp_decode) work on caller-owned buffers only:
+ *    they never allocate, free or synchronise; all GPU work is enqueued on
+ *    `stream` (a hipStream_t; NULL means the default stream) in call order.
+ *    No global mutable state: calls on different streams may run concurrently
+ *    if their buffers are disjoint.  The host-only calls (planners, arena,
+ *    exponent encoder) touch no GPU.  The pager (apmoe_pager_*) is the one
+ *    stateful object: its block below lists what it allocates and where it
+ *    waits on the host.
  *  - Pointers are device pointers unless marked [host].  fp16 values travel
  *    as uint16_t bit patterns (IEEE binary16).
  *  - T = 0 is a successful no-op.
@@ -84,7 +90,12 @@ typedef struct apmoe_expert {
 } apmoe_expert;
 
 /*
- * Router: logits[t][e] = scale * (sum_h x[t][h] * w_router[e][h] + bias[e]),
+ * Router: the top-k softmax gate of the MoE layer whose experts the bitwidth
+ * plan serves ("内存的饥饿游戏：当 MoE 权重与 KV 缓存争夺 GPU 的每一字节",
+ * zhichai.net, section "三层感知：离线 + 路由 + 提示词": the router's choices are
+ * what the planner watches; the pages give no formula, so the plain top-k
+ * softmax is read):
+ * logits[t][e] = scale * (sum_h x[t][h] * w_router[e][h] + bias[e]),
  * products and sums in float64; the top k experts by logit (ties to the lower
  * index), listed by descending logit; gates = softmax over the k chosen logits.
  *  x        fp16 [T][H]          w_router fp32 [E][H]
@@ -120,7 +131,12 @@ int apmoe_route_stats(const uint16_t* x, int T, int H, const int32_t* topk_ids, 
                       int E, float* mass, float* wnorm, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Group slots by expert (stable: within an expert, slots in ascending order).
+ * Group slots by expert, so that each expert streams its bit-planes once for
+ * all the tokens routed to it (the per-expert bitwidth of "内存的饥饿游戏：当 MoE
+ * 权重与 KV 缓存争夺 GPU 的每一字节", zhichai.net, section "核心洞察：权重也能分页"
+ * is a property of the expert, so its tokens are processed together): a
+ * histogram, a scan and a stable permute (within an expert, slots in
+ * ascending order).
  * Each token owns kk = k + n_shared slots.  n_shared >= 0 always-on experts
  * (a shared expert split into n_shared experts of the routed size, each taking
  * every token with weight 1) come first: slot t*kk + j is expert j for
@@ -139,7 +155,12 @@ int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int n_shared, in
                   size_t ws_bytes, void* stream);
 
 /*
- * One stage of every routed expert's FFN over its group of slots.
+ * One stage of every routed expert's FFN over its group of slots, reading each
+ * expert's weights at that expert's own bitwidth: the top b bit-planes plus
+ * the b-bit per-row lookup table, or the fp16 fallback
+ * ("内存的饥饿游戏：当 MoE 权重与 KV 缓存争夺 GPU 的每一字节", zhichai.net, section
+ * "核心洞察：权重也能分页": one stored weight set serves 3, 4, 5 or 6 bits, nested
+ * by bit-plane, with 16 bits as the fallback).
  *  stage APMOE_GATE_UP_SWIGLU (optionally | APMOE_ONLY_GEMV or | APMOE_ONLY_TILE):
  *        in = x fp16 [T][H]; the row for sorted position
  *        p is x[sorted_slots[p] / k]; out = A fp16 [S][I] in sorted order,
@@ -160,6 +181,10 @@ int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int n_shared, in
  *           bytes (split-K partial sums; 0 for shapes that never split K).
  *           Calls that share one workspace must not overlap.
  * The dispatch reads counts and bitwidths on the device: no host sync.
+ * Limits: the kernels address `in` and every weight matrix with 32-bit byte
+ * offsets, so T * H * 2 (gate/up) or T * k * I * 2 (down) bytes of input and
+ * H * I * 2 bytes per matrix must each stay below 2 GiB (APMOE_EINVAL
+ * otherwise); T * k <= 2^30.
  * An always-on shared expert whose intermediate size is n times I runs in the
  * same call as n extra fp16 experts (its gate/up row blocks and its down
  * column blocks) grouped by apmoe_permute with n_shared = n (pass E + n and
@@ -172,7 +197,12 @@ int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, const int8_t
                             int mfma_min_tokens, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Weighted combine, kk = k + n_shared slots per token (as apmoe_permute):
+ * Weighted combine of the experts' outputs into the layer output, the last
+ * step of the MoE layer whose experts run at mixed bitwidths ("内存的饥饿游戏：
+ * 当 MoE 权重与 KV 缓存争夺 GPU 的每一字节", zhichai.net, section "核心洞察：权重也能
+ * 分页"; the pages give no formula, the plain gate-weighted sum is read), in a
+ * fixed order with no atomics, kk = k + n_shared slots per token (as
+ * apmoe_permute):
  *   out[t][h] = sum_{j=0..k-1} topk_w[t][j] * Y[pos_of_slot[t*kk + n_shared + j]][h]
  *             + sum_{j=0..n_shared-1} Y[pos_of_slot[t*kk + j]][h]  (+ y_shared[t][h]),
  * summed in fp32 in that order, rounded once to fp16.
@@ -199,7 +229,30 @@ int apmoe_plan_bitwidths(int E, int L, const int8_t* levels, const double* harm,
                          int8_t* bits_out);
 
 /*
- * Commit a plan at a safe boundary: validates bits_host [host] int8 [E] and
+ * Planner inputs from routing statistics (host only).  The offline harm table
+ * is corrected per expert by what apmoe_route_stats measured
+ * ("内存的饥饿游戏：当 MoE 权重与 KV 缓存争夺 GPU 的每一字节", zhichai.net, section
+ * "三层感知：离线 + 路由 + 提示词": busy experts are protected, and a residual from
+ * routing-weighted input norms adjusts the offline sensitivity to the current
+ * prompt; no formula is given, the plain reading is):
+ *   load[e]  = mass[e] / mean over experts of mass
+ *   resid[e] = (wnorm[e] / mass[e]) / (sum of wnorm / sum of mass), 1 if mass[e] = 0
+ *   mult[e]  = load[e] * resid[e]            (1 everywhere if nothing was routed)
+ * in double precision, sums in index order.
+ *  mass, wnorm [host] fp32 [E] (>= 0, as apmoe_route_stats wrote them);
+ *  mult [host] double [E] (out).  APMOE_EINVAL for a negative or NaN input.
+ * apmoe_plan_routed runs apmoe_plan_bitwidths on harm[e][l] * mult[e] (same
+ * arguments and returns, plus mass and wnorm).
+ */
+int apmoe_harm_multipliers(int E, const float* mass, const float* wnorm, double* mult);
+int apmoe_plan_routed(int E, int L, const int8_t* levels, const double* harm, const uint64_t* bytes,
+                      const int8_t* floor_bits, uint64_t budget, const float* mass, const float* wnorm,
+                      int8_t* bits_out);
+
+/*
+ * Commit a plan at a safe boundary ("内存的饥饿游戏：当 MoE 权重与 KV 缓存争夺 GPU
+ * 的每一字节", zhichai.net, section "安全边界与异步搬运": a new bitwidth plan takes
+ * effect only between layer calls): validates bits_host [host] int8 [E] and
  * enqueues its copy into bits_dev on `stream`, so layer calls enqueued before
  * it see the old bitwidths and calls enqueued after it see the new ones.  The
  * values travel as kernel arguments: bits_host may be reused on return.
@@ -314,6 +367,14 @@ int apmoe_arena_stats(const apmoe_arena* arena, uint64_t* free_bytes, uint64_t* 
  *          device to device (any pointer may be NULL).
  *  destroy waits for outstanding copies and commits; the arena stays the
  *          caller's.
+ * Host resources and waits (the pager is the library's one stateful object):
+ * create allocates the pager, a pinned host patch buffer (hipHostMalloc) and
+ * two HIP events, all freed by destroy; a commit that retires blocks creates
+ * one more event, destroyed once those blocks are back in the arena.  stage
+ * waits on the host (hipEventSynchronize) for the previous commit to have run,
+ * and, when the arena is short, for the retired blocks; if enqueueing a copy
+ * fails it synchronises copy_stream before undoing the claims.  destroy waits
+ * for every outstanding copy and commit.
  * Needs 1 <= E <= APMOE_MAX_EXPERTS, H % 32 == 0, I % 32 == 0.
  */
 typedef struct apmoe_pager apmoe_pager;

@@ -144,3 +144,40 @@ def online_step(levels, harm, nbytes, floor_bits, stage_bits, m_total, m_kv, hys
                 return OK, bits, s, bits.tolist() != now
     last = stage_floors(len(stage_bits) - 1)
     return ENOSPACE, last, len(stage_bits) - 1, last.tolist() != now
+
+
+def harm_multipliers(mass, wnorm):
+    """Per-expert multipliers of the offline harm table from one router call's
+    routing statistics, float64.
+
+    The planner page ("内存的饥饿游戏…", zhichai.net, section "三层感知：离线 +
+    路由 + 提示词") protects experts that receive more routing and corrects the
+    offline sensitivity table with a residual taken from routing-weighted input
+    norms; it gives no formula.  Read plainly:
+        load[e]  = mass[e] / mean over experts of mass
+        resid[e] = (wnorm[e] / mass[e]) / (sum of wnorm / sum of mass)
+                   (1 for an expert with no routing mass)
+        mult[e]  = load[e] * resid[e]
+    and mult = 1 everywhere when nothing was routed.  Returns (mult, load, resid).
+    """
+    mass = [float(v) for v in mass]
+    wnorm = [float(v) for v in wnorm]
+    E = len(mass)
+    tot_m = sum(mass)
+    tot_n = sum(wnorm)
+    if not (tot_m > 0 and tot_n > 0):
+        return np.ones(E), np.ones(E), np.ones(E)
+    mean_m = tot_m / E
+    mean_norm = tot_n / tot_m
+    load = np.array([m / mean_m for m in mass])
+    resid = np.array([(n / m) / mean_norm if m > 0 else 1.0 for m, n in zip(mass, wnorm)])
+    return load * resid, load, resid
+
+
+def plan_routed(levels, harm, nbytes, floor_bits, budget, mass, wnorm):
+    """The greedy plan over the offline harm table scaled per expert by the
+    routing multipliers (harm'[e][l] = harm[e][l] * mult[e])."""
+    mult, _, _ = harm_multipliers(mass, wnorm)
+    scaled = np.asarray(harm, dtype=np.float64) * mult[:, None]
+    return plan_bitwidths(levels, scaled, nbytes, floor_bits, budget)
+

@@ -62,14 +62,6 @@ def layer_ref(inp, bits, tokens=None):
     return out
 
 
-PREFILL_SAMPLE = 48
-
-
-def prefill_tokens(T: int, n: int = PREFILL_SAMPLE, seed: int = 1234):
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(T, size=n, replace=False))
-
-
 def fill_all():
     import time
     for name in synth.CONFIG_ORDER:
@@ -77,8 +69,7 @@ def fill_all():
         t = time.time()
         inp = synth.make_inputs(cfg, seed=0)
         bits = resolve_bits(inp)
-        tokens = prefill_tokens(cfg.T) if cfg.T > 1024 else None
-        layer_ref(inp, bits, tokens)
+        layer_ref(inp, bits)
         print(f"{name}: {time.time() - t:.1f}s", flush=True)
 
 

@@ -15,7 +15,7 @@ from oracle import planner as planner_ref
 def test_library_exports_header_symbols():
     lib = _lib._lib()
     names = _lib.header_symbols()
-    assert len(names) == 26, names
+    assert len(names) == 28, names
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -82,6 +82,13 @@ def test_validation_before_launch():
     assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, 4, 64, 64, 0, None, 0, None) == _lib.EINVAL
     assert g(0, fake, fake, 8, fake, None, 2, fake, fake, 4, 64, 64, 16, None, 0, None) == _lib.EINVAL
     assert g(0, None, None, 8, None, None, 2, None, None, 0, 64, 64, 16, None, 0, None) == _lib.OK
+    # buffers past the kernels' 32-bit byte offsets are refused before any launch:
+    # x of T * H * 2 = 2 GiB (gate/up), A of T * k * I * 2 = 2 GiB (down), a
+    # 2 GiB fp16 matrix; one element less passes validation up to the workspace check
+    assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, 1 << 18, 4096, 64, 16, fake, big, None) == _lib.EINVAL
+    assert g(1, fake, fake, 8, fake, fake, 2, fake, fake, 1 << 16, 64, 8192, 16, fake, big, None) == _lib.EINVAL
+    assert g(1, fake, fake, 8, fake, fake, 2, fake, fake, 4, 32768, 32768, 16, fake, big, None) == _lib.EINVAL
+    assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, (1 << 18) - 1, 4096, 64, 16, fake, 0, None) == _lib.ENOSPACE
     # combine
     assert lib.apmoe_combine(fake, fake, fake, 4, 2, 0, 48, None, fake, None) == _lib.EINVAL
     assert lib.apmoe_combine(None, fake, fake, 4, 2, 0, 64, None, fake, None) == _lib.EINVAL

@@ -182,3 +182,37 @@ def test_paged_qwen_decode_full_size():
     G.check_out({"out": _forward(inp, layer)}, layer_ref(inp, bits1))
     G.say(f"  demoted {len(six)} experts; {pe.stats()}")
     pe.close()
+
+
+def test_online_planner_on_paged_layer_goes_through_the_pager():
+    """The online planner on a paged layer: every changed plan is staged by the
+    pager and committed with its planes and LUTs, so the next forward runs at
+    the new bitwidths on resident blocks (output against the oracle at those
+    bitwidths, blocks against the host copy), while the KV footprint grows and
+    then shrinks."""
+    from any_precision_quantized_amd.layer import OnlinePlanner
+    cfg = PAGED
+    bits0 = [6, 6, 6, 6, 6, 6]
+    inp, pe, layer = _paged(cfg, bits0)
+    levels = [6, 5, 4, 3]
+    nbytes = np.array([[paging_bytes(cfg, b) for b in levels]] * cfg.E, dtype=np.uint64)
+    harm = np.array([[0.0, 1.0, 3.0, 7.0]] * cfg.E) * (1 + np.arange(cfg.E))[:, None]
+    planner_ = OnlinePlanner(layer, levels, harm, nbytes, [3] * cfg.E, [5, 4, 3],
+                             m_total=int(nbytes[:, 0].sum()), hysteresis=0, bits_now=bits0)
+    step = int(nbytes[0, 0] - nbytes[0, 2])
+    seen = set()
+    for m_kv in (step, 3 * step, 6 * step, 2 * step, 0):
+        st, bits, stage, changed = planner_.step(m_kv=m_kv)
+        assert st == _lib.OK
+        G.say(f"  m_kv {m_kv}: bits {bits.tolist()} stage {stage} changed {changed}")
+        out = _forward(inp, layer)
+        _check_resident(pe, layer, bits)
+        G.check_out({"out": out}, moe.layer(inp, bits=bits))
+        seen.add(tuple(bits.tolist()))
+    assert len(seen) >= 3, "the sweep should move through several plans"
+    pe.close()
+
+
+def paging_bytes(cfg, b):
+    """Plane + LUT bytes of one expert's three matrices at b bits."""
+    return 3 * (cfg.H * cfg.I * b // 8) + (2 * cfg.I + cfg.H) * (1 << b) * 2

@@ -14,7 +14,7 @@ from any_precision_quantized_amd import _lib
 from oracle import moe
 
 from . import gpu_helpers as G
-from .oracle_cache import layer_ref, prefill_tokens, resolve_bits
+from .oracle_cache import layer_ref, resolve_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -134,23 +134,28 @@ FULL = ["tiny", "qwen_decode", "mixtral_decode_t1", "mixtral_decode_t8", "mixtra
         "e128_decode", "mixtral_prefill"]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_layer(name):
+    """Every output element of the full-size workload against the oracle
+    (the Mixtral-shaped prefill included: all 8192 x 4096 outputs), and the
+    expert stages in isolation on the hottest and the coldest touched expert
+    (A against the oracle on the same grouping, Y against the oracle fed with
+    the GPU's own A); at the prefill shape those groups of about 2048 slots
+    run on the MFMA tile path."""
     cfg = synth.get(name)
     G.say(f"full-size case {name}")
     inp = G.inputs(cfg)
     bits = resolve_bits(inp)
-    tokens = prefill_tokens(cfg.T) if cfg.T > 1024 else None
-    ref = layer_ref(inp, bits, tokens)
+    ref = layer_ref(inp, bits)
     _, got = G.run_layer(inp, bits)
     n_amb = G.check_route(inp, got, ref["ids"], ref["gates"], ref["logits"])
     G.check_grouping(cfg, got)
-    ratio = G.check_out(got, ref, tokens)
-    # per-expert isolation on two touched experts (hottest and coldest) of the smaller shapes
+    ratio = G.check_out(got, ref)
     touched = [e for e in range(cfg.E) if got["counts"][e] > 0]
-    if cfg.H * cfg.I <= 2048 * 2048:
-        G.check_experts(inp, bits, got, experts=[touched[0], touched[-1]])
-    G.say(f"  ambiguous routes {n_amb}, layer err/bound {ratio:.3g}, "
+    G.say(f"  layer err/bound {ratio:.3g} over all {cfg.T} tokens; checking experts {touched[0]}, {touched[-1]}")
+    worst = G.check_experts(inp, bits, got, experts=sorted({touched[0], touched[-1]}))
+    G.say(f"  ambiguous routes {n_amb}, expert err/bound {worst:.3g}, "
           f"groups {sorted(got['counts'].tolist(), reverse=True)[:8]}")
 
 

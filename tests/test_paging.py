@@ -167,3 +167,63 @@ def test_pager_create_argument_errors():
                 "apmoe_pager_stats": (None, None, None, None, None, None)}[fn]
         assert getattr(lib, fn)(*args) == _lib.EINVAL
     assert lib.apmoe_pager_destroy(None) == _lib.OK
+
+
+class _FakePager:
+    """Stands in for PagedExperts on the host: records the plans it is asked
+    to make resident and answers with a fixed status."""
+
+    def __init__(self, status):
+        self.status = status
+        self.applied = []
+
+    def apply(self, bits, stream=None):
+        self.applied.append([int(b) for b in bits])
+        return self.status
+
+
+class _HostLayer:
+    """The attributes MoELayer.commit and replan read, without device memory."""
+
+    def __init__(self, pager):
+        self.pager = pager
+        self.n_shared = 0
+        self.bits = None
+
+    commit = __import__("any_precision_quantized_amd.layer", fromlist=["MoELayer"]).MoELayer.commit
+
+
+def test_plans_on_paged_layer_go_through_the_pager(monkeypatch):
+    """With a pager attached, a commit (directly, or from the online planner)
+    stages the new residency through the pager instead of writing the bits
+    table alone, which would point the kernels at planes that are not
+    resident; when the pager cannot hold the plan the planner keeps its old
+    plan.  No GPU work is enqueued: the device bits write is replaced by a
+    trap."""
+    from any_precision_quantized_amd import layer as L
+
+    def no_direct_write(*a, **k):
+        raise AssertionError("bits table written without the pager")
+
+    monkeypatch.setattr(_lib, "commit_bits", no_direct_write)
+    ok = _FakePager(_lib.OK)
+    lay = _HostLayer(ok)
+    assert lay.commit([6, 5, 4]) == _lib.OK
+    assert ok.applied == [[6, 5, 4]]
+
+    levels = [6, 5, 4, 3]
+    nbytes = np.array([[600, 500, 400, 300]] * 3, dtype=np.uint64)
+    harm = np.array([[0.0, 1.0, 3.0, 7.0]] * 3) * np.array([[1.0], [2.0], [3.0]])
+    planner = L.OnlinePlanner(lay, levels, harm, nbytes, [3] * 3, [5, 4, 3], m_total=1800, hysteresis=0,
+                              bits_now=[6, 6, 6])
+    st, bits, stage, changed = planner.step(m_kv=400)          # budget 1400: a demotion is needed
+    assert st == _lib.OK and changed and ok.applied[-1] == bits.tolist()
+    assert planner.bits.tolist() == bits.tolist()
+
+    full = _FakePager(_lib.ENOSPACE)
+    lay2 = _HostLayer(full)
+    planner2 = L.OnlinePlanner(lay2, levels, harm, nbytes, [3] * 3, [5, 4, 3], m_total=1800, hysteresis=0,
+                               bits_now=[6, 6, 6])
+    st, bits, stage, changed = planner2.step(m_kv=400)
+    assert st == _lib.ENOSPACE and not changed
+    assert len(full.applied) == 1 and planner2.bits.tolist() == [6, 6, 6] and bits.tolist() == [6, 6, 6]

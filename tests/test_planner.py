@@ -109,38 +109,84 @@ def test_zipf_plan_keeps_hot_experts_high():
 # ---------------------------------------------------------------------------
 
 def test_harm_multipliers_hand_values():
-    from any_precision_quantized_amd.layer import harm_multipliers
     # equal input norms (2): the residual is 1 everywhere and the multiplier is
     # the expert's share of routing against an even 3/4 per expert
-    mult, load, resid = harm_multipliers([0.8, 0.8, 1.4, 0.0], [1.6, 1.6, 2.8, 0.0])
+    mult, load, resid = planner.harm_multipliers([0.8, 0.8, 1.4, 0.0], [1.6, 1.6, 2.8, 0.0])
     np.testing.assert_allclose(load, [16 / 15, 16 / 15, 28 / 15, 0.0], rtol=1e-15)
     np.testing.assert_allclose(resid, [1.0, 1.0, 1.0, 1.0], rtol=1e-15)
     np.testing.assert_allclose(mult, load, rtol=1e-15)
     # equal routing, inputs of norm 1 and 3: residuals 1/2 and 3/2 of the mean 2
-    mult, load, resid = harm_multipliers([1.0, 1.0], [1.0, 3.0])
-    np.testing.assert_allclose(load, [1.0, 1.0])
-    np.testing.assert_allclose(resid, [0.5, 1.5])
-    np.testing.assert_allclose(mult, [0.5, 1.5])
+    mult, load, resid = planner.harm_multipliers([1.0, 1.0], [1.0, 3.0])
+    assert load.tolist() == [1.0, 1.0] and resid.tolist() == [0.5, 1.5] and mult.tolist() == [0.5, 1.5]
     # nothing routed: the offline table stands
-    mult, _, _ = harm_multipliers([0.0, 0.0, 0.0], [0.0, 0.0, 0.0])
-    np.testing.assert_allclose(mult, [1.0, 1.0, 1.0])
+    mult, _, _ = planner.harm_multipliers([0.0, 0.0, 0.0], [0.0, 0.0, 0.0])
+    assert mult.tolist() == [1.0, 1.0, 1.0]
 
 
-def test_harm_multipliers_demote_idle_experts_first():
+def test_native_harm_multipliers_match_oracle():
+    """apmoe_harm_multipliers through the C ABI: the hand values exactly, and the
+    oracle bit for bit on routing statistics of random routings (same formula,
+    sums in the same index order, float64)."""
     from any_precision_quantized_amd import _lib
-    from any_precision_quantized_amd.layer import harm_multipliers
+    assert _lib.harm_multipliers([1.0, 1.0], [1.0, 3.0]).tolist() == [0.5, 1.5]
+    assert _lib.harm_multipliers([0.0, 0.0, 0.0], [0.0, 0.0, 0.0]).tolist() == [1.0, 1.0, 1.0]
+    # inputs rounded to fp32 as the device hands them over (0.8 is not exact)
+    np.testing.assert_allclose(_lib.harm_multipliers([0.8, 0.8, 1.4, 0.0], [1.6, 1.6, 2.8, 0.0]),
+                               [16 / 15, 16 / 15, 28 / 15, 0.0], rtol=1e-7)
+    from oracle import moe
+    rng = np.random.default_rng(7)
+    for trial in range(10):
+        T, E, k, H = int(rng.integers(1, 40)), int(rng.integers(2, 70)), 2, 64
+        x = rng.normal(size=(T, H)).astype(np.float16)
+        w = rng.normal(0, 0.02, size=(E, H)).astype(np.float32)
+        ids, gates, _ = moe.route(x, w, None, 1.0, k)
+        mass, wnorm = moe.route_stats(x, ids, gates, E)
+        mass, wnorm = mass.astype(np.float32), wnorm.astype(np.float32)   # what the device hands over
+        ref, _, _ = planner.harm_multipliers(mass, wnorm)
+        assert np.array_equal(_lib.harm_multipliers(mass, wnorm), ref)
+    for bad in (([1.0, -1.0], [1.0, 1.0]), ([1.0, float("nan")], [1.0, 1.0])):
+        with pytest.raises(_lib.ApmoeError):
+            _lib.harm_multipliers(*bad)
+
+
+def test_routed_plan_demotes_idle_experts_first():
+    """The routed plan (offline harm scaled by the routing multipliers): with
+    the same offline table for every expert, the expert nobody routes to goes
+    first, to its floor; native and oracle agree."""
+    from any_precision_quantized_amd import _lib
     levels = np.array([6, 5, 4, 3], np.int8)
     E = 4
     harm = np.tile(np.array([0.0, 2.0 ** -5, 2.0 ** -4, 2.0 ** -3]), (E, 1))   # the same offline table
     nbytes = np.tile(np.array([600, 500, 400, 300], np.uint64), (E, 1))
     floors = np.full(E, 3, np.int8)
-    mult, _, _ = harm_multipliers([1.5, 0.0, 1.0, 1.5], [3.0, 0.0, 2.0, 3.0])
+    mass, wnorm = [1.5, 0.0, 1.0, 1.5], [3.0, 0.0, 2.0, 3.0]
     budget = 4 * 600 - 300          # room for one expert at 3 bits
-    st, bits = _lib.plan_bitwidths(levels, harm * mult[:, None], nbytes, floors, budget)
+    st, bits = _lib.plan_routed(levels, harm, nbytes, floors, budget, mass, wnorm)
     assert st == _lib.OK
-    assert bits.tolist() == [6, 3, 6, 6]   # the expert nobody routes to goes first, to its floor
-    st, ref = planner.plan_bitwidths(levels, harm * mult[:, None], nbytes, floors, budget)
+    assert bits.tolist() == [6, 3, 6, 6]
+    st, ref = planner.plan_routed(levels, harm, nbytes, floors, budget, mass, wnorm)
     assert st == planner.OK and ref.tolist() == bits.tolist()
+
+
+def test_native_routed_plan_matches_oracle():
+    from any_precision_quantized_amd import _lib
+    rng = np.random.default_rng(11)
+    levels = [6, 5, 4, 3]
+    for trial in range(20):
+        E = int(rng.integers(1, 60))
+        size = rng.integers(1000, 10**7, size=E)
+        nb = np.array([[int(sz * b / 16) + 31 for b in levels] for sz in size], dtype=np.uint64)
+        harm = np.cumsum(rng.random((E, 4)), axis=1)
+        harm -= harm[:, :1]
+        floors = np.full(E, 3, np.int8)
+        mass = (rng.random(E) * (rng.random(E) > 0.3)).astype(np.float32)
+        wnorm = (mass * rng.uniform(20, 60, size=E)).astype(np.float32)
+        lo = planner.plan_total(levels, nb, floors)
+        hi = planner.plan_total(levels, nb, [6] * E)
+        for budget in np.linspace(lo, hi, 5).astype(np.int64):
+            st_ref, ref = planner.plan_routed(levels, harm, nb, floors, int(budget), mass, wnorm)
+            st, bits = _lib.plan_routed(levels, harm, nb, floors, int(budget), mass, wnorm)
+            assert st == st_ref and np.array_equal(bits, ref)
 
 
 # ---------------------------------------------------------------------------
