@@ -49,6 +49,8 @@ def _lib():
             "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp],
             "apmoe_bitplane_lut_gemm": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                         _c_int, _c_int, _c_int, _vp, _c_size, _vp],
+            "apmoe_bitplane_lut_gemm_noalloc": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
+                                                _c_int, _c_int, _c_int, _vp],
             "apmoe_combine": [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp],
             "apmoe_plan_bitwidths": [_c_int, _c_int, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp],
             "apmoe_plan_online": [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, ctypes.c_uint64,
@@ -213,6 +215,25 @@ def bitplane_lut_gemm(stage, experts_desc, bits, E, offsets, sorted_slots, k, in
         k, inp.data_ptr(), out.data_ptr(), T, H, I, int(mfma_min_tokens),
         None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream))
     _check(rc, "apmoe_bitplane_lut_gemm")
+
+
+def bitplane_lut_gemm_noalloc(stage, experts_desc, bits, E, offsets, sorted_slots, k, inp, out, T, H, I,
+                              mfma_min_tokens, stream=None):
+    """apmoe_bitplane_lut_gemm_noalloc: the same stage with the library's static scratch."""
+    torch = _torch()
+    S = T * k
+    base = stage & ~(ONLY_GEMV | ONLY_TILE)
+    if base == GATE_UP_SWIGLU:
+        _ptr(inp, torch.float16, T * H, "x")
+        _ptr(out, torch.float16, S * I, "A")
+    elif base == DOWN:
+        _ptr(inp, torch.float16, S * I, "A")
+        _ptr(out, torch.float32, S * H, "Y")
+    rc = _lib().apmoe_bitplane_lut_gemm_noalloc(
+        int(stage), _ptr(experts_desc, torch.int64, E * 18, "experts"), _ptr(bits, torch.int8, E, "bits"), E,
+        _ptr(offsets, torch.int32, E + 1, "offsets"), _ptr(sorted_slots, torch.int32, None, "sorted_slots"),
+        k, inp.data_ptr(), out.data_ptr(), T, H, I, int(mfma_min_tokens), _stream(stream))
+    _check(rc, "apmoe_bitplane_lut_gemm_noalloc")
 
 
 def combine(Y, pos_of_slot, topk_w, T, k, H, y_shared, out, n_shared=0, stream=None):

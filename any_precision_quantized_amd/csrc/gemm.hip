@@ -6,6 +6,7 @@
 // the other path, so no count ever travels to the host.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -358,10 +359,14 @@ int launch_tile(const GemmArgs& a, hipStream_t s) {
 
 using namespace apmoe;
 
-extern "C" int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, const int8_t* bits,
-                                       int E, const int32_t* offsets, const int32_t* sorted_slots,
-                                       int k, const uint16_t* in, void* out, int T, int H, int I,
-                                       int mfma_min_tokens, void* ws, size_t ws_bytes, void* stream) {
+namespace apmoe {
+namespace {
+
+// Validation and dispatch shared by both entry points; ws may be NULL when the
+// shapes never split K (apmoe_workspace_bytes says how much a call needs).
+int gemm_call(int stage, const apmoe_expert* experts, const int8_t* bits, int E, const int32_t* offsets,
+              const int32_t* sorted_slots, int k, const uint16_t* in, void* out, int T, int H, int I,
+              int mfma_min_tokens, void* ws, size_t ws_bytes, size_t ws_need, void* stream) {
     const int paths = stage & (APMOE_ONLY_GEMV | APMOE_ONLY_TILE);
     stage &= ~(APMOE_ONLY_GEMV | APMOE_ONLY_TILE);
     if (stage != APMOE_GATE_UP_SWIGLU && stage != APMOE_DOWN) return APMOE_EINVAL;
@@ -377,7 +382,7 @@ extern "C" int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, c
     if (T == 0) return APMOE_OK;
     if (!experts || !bits || !offsets || !in || !out) return APMOE_EINVAL;
     if (stage == APMOE_GATE_UP_SWIGLU && !sorted_slots) return APMOE_EINVAL;
-    if (ws_bytes < apmoe_workspace_bytes(T, k, E, H, I)) return APMOE_ENOSPACE;
+    if (ws_bytes < ws_need) return APMOE_ENOSPACE;
     // A token holds at most one slot of each expert, so no group exceeds T
     // slots: below the threshold every group takes the GEMV path and the tile
     // launch is skipped (the effective threshold keeps that true for any
@@ -391,4 +396,66 @@ extern "C" int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, c
     }
     if (paths != APMOE_ONLY_GEMV) return launch_tile(a, s);
     return APMOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the split-K partial sums live
+// in this file-scope device array (one copy per GPU, held until the process
+// ends).  Host code never passes the array's name to a kernel: on the host it
+// is only a stand-in for the symbol.  Its device address is looked up once per
+// device (hipGetSymbolAddress with that device current) and that address is
+// what the kernels receive.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)APMOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch, or NULL on a HIP error.
+void* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Scratch bytes one stage needs (the split-K partial sums of its GEMV launch).
+size_t noalloc_need(int stage, int T, int k, int E, int H, int I) {
+    if (T <= 0 || k < 1 || E < 1 || H <= 0 || I <= 0) return 0;
+    const bool gu = (stage & ~(APMOE_ONLY_GEMV | APMOE_ONLY_TILE)) == APMOE_GATE_UP_SWIGLU;
+    return gu ? gemv_workspace_bytes(T, k, E, I, H, 2) : gemv_workspace_bytes(T, k, E, H, I, 1);
+}
+
+}  // namespace
+}  // namespace apmoe
+
+extern "C" int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, const int8_t* bits,
+                                       int E, const int32_t* offsets, const int32_t* sorted_slots,
+                                       int k, const uint16_t* in, void* out, int T, int H, int I,
+                                       int mfma_min_tokens, void* ws, size_t ws_bytes, void* stream) {
+    const size_t need = (T > 0 && E >= 1 && k >= 1 && H > 0 && I > 0) ? apmoe_workspace_bytes(T, k, E, H, I) : 0;
+    return gemm_call(stage, experts, bits, E, offsets, sorted_slots, k, in, out, T, H, I, mfma_min_tokens, ws,
+                     ws_bytes, need, stream);
+}
+
+extern "C" int apmoe_bitplane_lut_gemm_noalloc(int stage, const apmoe_expert* experts, const int8_t* bits,
+                                               int E, const int32_t* offsets, const int32_t* sorted_slots,
+                                               int k, const uint16_t* in, void* out, int T, int H, int I,
+                                               int mfma_min_tokens, void* stream) {
+    const size_t need = noalloc_need(stage, T, k, E, H, I);
+    if (need > kScratchBytes) return APMOE_ENOSPACE;   // beyond the fixed scratch: use apmoe_bitplane_lut_gemm
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_on_current_device();
+        if (!ws) return APMOE_EHIP;
+    }
+    return gemm_call(stage, experts, bits, E, offsets, sorted_slots, k, in, out, T, H, I, mfma_min_tokens, ws,
+                     need > 0 ? kScratchBytes : 0, need, stream);
 }

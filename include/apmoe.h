@@ -197,6 +197,26 @@ int apmoe_bitplane_lut_gemm(int stage, const apmoe_expert* experts, const int8_t
                             int mfma_min_tokens, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * apmoe_bitplane_lut_gemm for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as apmoe_bitplane_lut_gemm, without a workspace: the
+ * split-K partial sums live in a static device array of
+ * APMOE_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends; its address is looked up once per device on the first call).
+ * The call allocates nothing.  It returns APMOE_ENOSPACE when the stage needs
+ * more scratch than that (apmoe_workspace_bytes bounds the need; every shape
+ * whose K is not split needs none) and APMOE_EHIP if the scratch address
+ * cannot be looked up.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (on different streams) race; calls ordered on one
+ * stream do not.
+ */
+#define APMOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int apmoe_bitplane_lut_gemm_noalloc(int stage, const apmoe_expert* experts, const int8_t* bits, int E,
+                                    const int32_t* offsets, const int32_t* sorted_slots, int k,
+                                    const uint16_t* in, void* out, int T, int H, int I,
+                                    int mfma_min_tokens, void* stream);
+
+/*
  * Weighted combine of the experts' outputs into the layer output, the last
  * step of the MoE layer whose experts run at mixed bitwidths ("内存的饥饿游戏：
  * 当 MoE 权重与 KV 缓存争夺 GPU 的每一字节", zhichai.net, section "核心洞察：权重也能

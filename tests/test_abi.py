@@ -15,7 +15,7 @@ from oracle import planner as planner_ref
 def test_library_exports_header_symbols():
     lib = _lib._lib()
     names = _lib.header_symbols()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -89,6 +89,13 @@ def test_validation_before_launch():
     assert g(1, fake, fake, 8, fake, fake, 2, fake, fake, 1 << 16, 64, 8192, 16, fake, big, None) == _lib.EINVAL
     assert g(1, fake, fake, 8, fake, fake, 2, fake, fake, 4, 32768, 32768, 16, fake, big, None) == _lib.EINVAL
     assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, (1 << 18) - 1, 4096, 64, 16, fake, 0, None) == _lib.ENOSPACE
+    # the allocation-free stage refuses shapes whose split-K partials exceed its
+    # static scratch before touching the GPU: 16384 tokens over 4 experts of 64
+    # rows, K = 14336 split in 4: 4 * 16384 * 2 * 64 * 4 bytes = 32 MiB > 16 MiB
+    na = lib.apmoe_bitplane_lut_gemm_noalloc
+    assert na(0, fake, fake, 4, fake, fake, 1, fake, fake, 16384, 14336, 64, 1 << 30, None) == _lib.ENOSPACE
+    assert na(7, fake, fake, 8, fake, fake, 2, fake, fake, 4, 64, 64, 16, None) == _lib.EINVAL
+    assert na(0, None, None, 8, None, None, 2, None, None, 0, 64, 64, 16, None) == _lib.OK
     # combine
     assert lib.apmoe_combine(fake, fake, fake, 4, 2, 0, 48, None, fake, None) == _lib.EINVAL
     assert lib.apmoe_combine(None, fake, fake, 4, 2, 0, 64, None, fake, None) == _lib.EINVAL
