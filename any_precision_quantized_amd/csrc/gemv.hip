@@ -110,49 +110,68 @@ struct Item {
 };
 
 // Item of workgroup `idx`: experts on this path each own ceil(rows / 64) row
-// blocks times KS splits, in expert order.  Every wave finds it on its own
-// (a wave-wide scan over the slot counts); returns false past the last item.
+// blocks times KS splits, in expert order.  Every wave finds it on its own:
+// the slot counts and bitwidths of all experts (up to four chunks of 64) are
+// loaded at once and a wave-wide scan per chunk numbers the items; returns
+// false past the last item.
 //
-// With one K split, at most 64 experts and between 2 and 3 items per CU, ncu
-// is the CU count: the dispatcher places workgroups b, b + ncu and b + 2 ncu
-// on one CU, so the first N - 2 ncu block numbers land on the CUs that hold
-// three items.  The items are then rotated so that those blocks take the last
-// items (the least routed experts, the cheapest) and the head of the expert
-// order (fp16 always-on experts, the most routed ones) lands on CUs that hold
-// two.  With at most 64 experts one wave-wide scan gives both the total and
-// the item, so the rotation costs no extra load.
+// With ROT, one K split, at most 64 experts and between 2 and 3 items per CU,
+// ncu is the CU count: the dispatcher places workgroups b, b + ncu and
+// b + 2 ncu on one CU, so the first N - 2 ncu block numbers land on the CUs
+// that hold three items.  The items are then rotated so that those blocks
+// take the last items (the least routed experts, the cheapest) and the head of
+// the expert order (fp16 always-on experts, the most routed ones) lands on CUs
+// that hold two.
+constexpr int kMaxChunks = APMOE_MAX_EXPERTS / kWave;
+
+template <bool ROT>
 __device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, int idx, int ncu, Item& it) {
     const int lane = threadIdx.x % kWave;
-    int base = 0;
-    for (int c0 = 0; c0 < a.E; c0 += kWave) {
-        const int e = c0 + lane;
-        int m = 0, b = 0;
-        if (e < a.E) {
-            m = a.offsets[e + 1] - a.offsets[e];
-            b = a.bits[e];
+    const int nch = (a.E + kWave - 1) / kWave;
+    int m[kMaxChunks], b[kMaxChunks], n[kMaxChunks], inc[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        m[c] = 0;
+        b[c] = 0;
+        const int e = c * kWave + lane;
+        if (c < nch && e < a.E) {
+            m[c] = a.offsets[e + 1] - a.offsets[e];
+            b[c] = a.bits[e];
         }
-        const int n = (m > 0 && m < a.mfma_min_tokens && valid_bits(b)) ? nrb : 0;
-        const int inc = wave_incl_scan(n);
-        if (c0 == 0 && KS == 1 && a.E <= kWave) {
-            const int total = __builtin_amdgcn_readlane(inc, kWave - 1);
-            if (idx >= total) return false;
+    }
+    int total = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        n[c] = (m[c] > 0 && m[c] < a.mfma_min_tokens && valid_bits(b[c])) ? nrb : 0;
+        inc[c] = 0;
+        if (c < nch) {   // uniform
+            inc[c] = wave_incl_scan(n[c]) + total;
+            total = __builtin_amdgcn_readlane(inc[c], kWave - 1);
+        }
+    }
+    if (idx >= total * KS) return false;
+    if constexpr (ROT) {
+        if (KS == 1 && a.E <= kWave) {
             const int three = total - 2 * ncu;   // CUs that hold a third item
             if (three > 0 && three <= ncu) idx = (idx - three + total) % total;
         }
-        const int blk = idx / KS;
-        const int first = base + inc - n;
-        const unsigned long long hit = __ballot(n > 0 && blk >= first && blk < first + n);
+    }
+    const int blk = idx / KS;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        if (c >= nch) break;   // uniform
+        const int first = inc[c] - n[c];
+        const unsigned long long hit = __ballot(n[c] > 0 && blk >= first && blk < first + n[c]);
         if (hit) {
             const int src = __ffsll((long long)hit) - 1;
-            it.e = __builtin_amdgcn_readfirstlane(c0 + src);
-            it.m = __builtin_amdgcn_readlane(m, src);
-            it.b = __builtin_amdgcn_readlane(b, src);
+            it.e = __builtin_amdgcn_readfirstlane(c * kWave + src);
+            it.m = __builtin_amdgcn_readlane(m[c], src);
+            it.b = __builtin_amdgcn_readlane(b[c], src);
             it.rb = blk - __builtin_amdgcn_readlane(first, src);
             it.off = a.offsets[it.e];
             it.ks = idx % KS;
             return true;
         }
-        base += __builtin_amdgcn_readlane(inc, kWave - 1);
     }
     return false;
 }
@@ -576,7 +595,7 @@ void gemv_kernel(GemmArgs a, int KS, float* partial, int ncu) {
     sh.in_bytes = (uint32_t)((NMAT == 2 ? (size_t)a.T : (size_t)sh.S) * sh.K * 2);
 
     Item it;
-    if (!find_item(a, (sh.rows + kItemRows - 1) / kItemRows, KS, blockIdx.x, ncu, it)) return;   // uniform
+    if (!find_item<true>(a, (sh.rows + kItemRows - 1) / kItemRows, KS, blockIdx.x, ncu, it)) return;   // uniform
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
