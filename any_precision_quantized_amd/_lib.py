@@ -43,10 +43,11 @@ def _lib():
                                "`python -m any_precision_quantized_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
         sig = {
-            "apmoe_route": [_vp, _c_int, _c_int, _vp, _vp, ctypes.c_float, _c_int, _c_int, _vp, _vp, _vp,
+            "apmoe_route": [_vp, _c_int, _c_int, _vp, _vp, ctypes.c_float, _c_int, _c_int, _vp, _vp, _vp, _vp,
                             _c_size, _vp],
             "apmoe_route_stats": [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp],
-            "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp],
+            "apmoe_permute": [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _c_size, _vp],
             "apmoe_bitplane_lut_gemm": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
                                         _c_int, _c_int, _c_int, _vp, _c_size, _vp],
             "apmoe_bitplane_lut_gemm_noalloc": [_c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int,
@@ -70,7 +71,7 @@ def _lib():
             "apmoe_pager_create": [_c_int, _c_int, _c_int, _vp, _vp, _vp, _u64, _vp, _vp, _vp],
             "apmoe_pager_stage": [_vp, _vp, _vp],
             "apmoe_pager_commit": [_vp, _vp],
-            "apmoe_pager_stats": [_vp, _vp, _vp, _vp, _vp, _vp],
+            "apmoe_pager_stats": [_vp, _vp, _vp, _vp, _vp, _vp, _vp],
             "apmoe_pager_destroy": [_vp],
             "apmoe_exp_plan": [_vp, _u64, _vp, _vp, _vp],
             "apmoe_exp_encode": [_vp, _u64, _vp, _vp, _u64, _vp, _vp, _vp],
@@ -138,7 +139,7 @@ def _stream(stream=None):
 # Entry points (same names as the C ABI, without the prefix)
 # ---------------------------------------------------------------------------
 
-def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, ws=None, stream=None):
+def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, ws=None, stream=None, x_norms=None):
     torch = _torch()
     T, H = x.shape
     E = w_router.shape[0]
@@ -147,7 +148,8 @@ def route(x, w_router, bias, logit_scale, k, topk_ids, topk_w, ws=None, stream=N
                             _ptr(w_router, torch.float32, E * H, "w_router"),
                             _ptr(bias, torch.float32, E, "bias"), float(logit_scale), E, k,
                             _ptr(topk_ids, torch.int32, T * k, "topk_ids"),
-                            _ptr(topk_w, torch.float32, T * k, "topk_w"), wsp, wsb, _stream(stream))
+                            _ptr(topk_w, torch.float32, T * k, "topk_w"),
+                            _ptr(x_norms, torch.float32, T, "x_norms"), wsp, wsb, _stream(stream))
     _check(rc, "apmoe_route")
 
 
@@ -164,17 +166,25 @@ def route_stats(x, topk_ids, topk_w, E, mass, wnorm, ws, stream=None):
     _check(rc, "apmoe_route_stats")
 
 
-def permute(topk_ids, E, counts, offsets, sorted_slots, pos_of_slot, n_shared=0, stream=None):
+def permute(topk_ids, E, counts, offsets, sorted_slots, pos_of_slot, n_shared=0, stream=None, stats=None):
     """Grouping over E + n_shared experts and T * (k + n_shared) slots (the
-    n_shared always-on experts first)."""
+    n_shared always-on experts first).  stats: optional (topk_w, x_norms, mass,
+    wnorm, ws) for the routing statistics in the same launch."""
     torch = _torch()
     T, k = topk_ids.shape
     S = T * (k + n_shared)
+    tw = xn = ms = wn = wsp = None
+    wsb = 0
+    if stats is not None:
+        w_, n_, m_, v_, ws = stats
+        tw, xn = _ptr(w_, torch.float32, T * k, "topk_w"), _ptr(n_, torch.float32, T, "x_norms")
+        ms, wn = _ptr(m_, torch.float32, E, "mass"), _ptr(v_, torch.float32, E, "wnorm")
+        wsp, wsb = _ptr(ws, torch.uint8, S * 8, "ws"), ws.numel()
     rc = _lib().apmoe_permute(_ptr(topk_ids, torch.int32, T * k, "topk_ids"), T, k, E, n_shared,
                               _ptr(counts, torch.int32, E + n_shared, "counts"),
                               _ptr(offsets, torch.int32, E + n_shared + 1, "offsets"),
                               _ptr(sorted_slots, torch.int32, S, "sorted_slots"),
-                              _ptr(pos_of_slot, torch.int32, S, "pos_of_slot"), None, 0,
+                              _ptr(pos_of_slot, torch.int32, S, "pos_of_slot"), tw, xn, ms, wn, wsp, wsb,
                               _stream(stream))
     _check(rc, "apmoe_permute")
 
@@ -415,10 +425,10 @@ class Pager:
         _check(_lib().apmoe_pager_commit(self._h, _stream(stream)), "apmoe_pager_commit")
 
     def stats(self):
-        """dict: resident, free, largest_free, h2d, d2d (bytes)."""
-        v = [ctypes.c_uint64() for _ in range(5)]
+        """dict: resident, free, largest_free, h2d, d2d (bytes), ranges (copied by the last stage)."""
+        v = [ctypes.c_uint64() for _ in range(6)]
         _check(_lib().apmoe_pager_stats(self._h, *[ctypes.byref(x) for x in v]), "apmoe_pager_stats")
-        return dict(zip(("resident", "free", "largest_free", "h2d", "d2d"), (x.value for x in v)))
+        return dict(zip(("resident", "free", "largest_free", "h2d", "d2d", "ranges"), (x.value for x in v)))
 
     def close(self):
         h = getattr(self, "_h", None)

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libapmoe.so")
 ARCH = os.environ.get("APMOE_ARCH", "gfx950")
 
 HIP_SOURCES = ["route.hip", "permute.hip", "gemv.hip", "gemm.hip", "combine.hip", "pager.hip", "exp_decode.hip"]
-CXX_SOURCES = ["planner.cpp", "exp_encode.cpp"]
+CXX_SOURCES = ["planner.cpp", "exp_encode.cpp", "arena.cpp"]
 
 
 def _hipcc() -> str:
@@ -57,7 +57,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
-        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", "-c",
+        cmds.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}", "-c",
                      os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:

@@ -128,14 +128,16 @@ template <bool ROT>
 __device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, int idx, int ncu, Item& it) {
     const int lane = threadIdx.x % kWave;
     const int nch = (a.E + kWave - 1) / kWave;
-    int m[kMaxChunks], b[kMaxChunks], n[kMaxChunks], inc[kMaxChunks];
+    int o[kMaxChunks], m[kMaxChunks], b[kMaxChunks], n[kMaxChunks], inc[kMaxChunks];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
+        o[c] = 0;
         m[c] = 0;
         b[c] = 0;
         const int e = c * kWave + lane;
         if (c < nch && e < a.E) {
-            m[c] = a.offsets[e + 1] - a.offsets[e];
+            o[c] = a.offsets[e];
+            m[c] = a.offsets[e + 1] - o[c];
             b[c] = a.bits[e];
         }
     }
@@ -168,7 +170,7 @@ __device__ __forceinline__ bool find_item(const GemmArgs& a, int nrb, int KS, in
             it.m = __builtin_amdgcn_readlane(m[c], src);
             it.b = __builtin_amdgcn_readlane(b[c], src);
             it.rb = blk - __builtin_amdgcn_readlane(first, src);
-            it.off = a.offsets[it.e];
+            it.off = __builtin_amdgcn_readlane(o[c], src);   // no second, dependent load
             it.ks = idx % KS;
             return true;
         }

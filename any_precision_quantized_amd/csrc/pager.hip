@@ -9,6 +9,11 @@
 // the compute stream (a commit between two layer calls), and memory a commit
 // retires is reused only after every kernel enqueued before it has finished.
 //
+// The copies of one re-plan run on the copy engines (one hipMemcpyAsync per
+// range on the copy stream), so no compute unit takes part: a gather kernel
+// that read the pinned host copy over the bus was measured, and its
+// long-latency reads slowed the layer running beside it by about 40%.
+//
 // Device memory is one caller-owned arena carved by a host-side first-fit
 // allocator (apmoe_arena_*).  A matrix's resident planes are one block holding
 // planes 0..b-1 back to back at the packed slab stride, so the kernels'
@@ -23,132 +28,9 @@
 #include <vector>
 
 #include "common.hpp"
-
-namespace apmoe {
-namespace {
-
-constexpr uint64_t kAlign = 256;
-
-inline uint64_t align_up(uint64_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
-
-}  // namespace
-}  // namespace apmoe
+#include "residency.hpp"
 
 using namespace apmoe;
-
-// ---------------------------------------------------------------------------
-// Arena: free ranges of a [0, size) address range, kept coalesced.
-// ---------------------------------------------------------------------------
-
-struct apmoe_arena {
-    uint64_t size = 0;
-    std::map<uint64_t, uint64_t> free_;   // offset -> length, disjoint, never adjacent
-
-    // First fit in offset order.
-    bool alloc(uint64_t bytes, uint64_t* off) {
-        bytes = align_up(bytes);
-        for (auto it = free_.begin(); it != free_.end(); ++it) {
-            if (it->second < bytes) continue;
-            *off = it->first;
-            const uint64_t rest = it->second - bytes;
-            const uint64_t at = it->first + bytes;
-            free_.erase(it);
-            if (rest) free_[at] = rest;
-            return true;
-        }
-        return false;
-    }
-
-    // Claim exactly [off, off + bytes) if all of it is free.
-    bool take(uint64_t off, uint64_t bytes) {
-        bytes = align_up(bytes);
-        if (bytes == 0) return true;
-        auto it = free_.upper_bound(off);
-        if (it == free_.begin()) return false;
-        --it;
-        const uint64_t lo = it->first, hi = it->first + it->second;
-        if (off < lo || off + bytes > hi) return false;
-        free_.erase(it);
-        if (off > lo) free_[lo] = off - lo;
-        if (off + bytes < hi) free_[off + bytes] = hi - off - bytes;
-        return true;
-    }
-
-    // Return [off, off + bytes); false (and no change) if any of it is
-    // outside the arena or already free.
-    bool release(uint64_t off, uint64_t bytes) {
-        bytes = align_up(bytes);
-        if (bytes == 0) return true;
-        if (off % kAlign || off > size || bytes > size - off) return false;
-        auto next = free_.lower_bound(off);
-        if (next != free_.end() && next->first < off + bytes) return false;
-        if (next != free_.begin()) {
-            auto prev = std::prev(next);
-            if (prev->first + prev->second > off) return false;
-        }
-        uint64_t lo = off, len = bytes;
-        if (next != free_.begin()) {
-            auto prev = std::prev(next);
-            if (prev->first + prev->second == off) {
-                lo = prev->first;
-                len += prev->second;
-                free_.erase(prev);
-            }
-        }
-        next = free_.lower_bound(off);
-        if (next != free_.end() && next->first == off + bytes) {
-            len += next->second;
-            free_.erase(next);
-        }
-        free_[lo] = len;
-        return true;
-    }
-
-    void stats(uint64_t* free_bytes, uint64_t* largest, int* n) const {
-        uint64_t f = 0, l = 0;
-        for (const auto& r : free_) {
-            f += r.second;
-            l = std::max(l, r.second);
-        }
-        if (free_bytes) *free_bytes = f;
-        if (largest) *largest = l;
-        if (n) *n = (int)free_.size();
-    }
-};
-
-extern "C" int apmoe_arena_create(uint64_t bytes, apmoe_arena** out) {
-    if (!out) return APMOE_EINVAL;
-    *out = nullptr;
-    apmoe_arena* a = new (std::nothrow) apmoe_arena();
-    if (!a) return APMOE_ENOSPACE;
-    a->size = bytes / kAlign * kAlign;
-    if (a->size) a->free_[0] = a->size;
-    *out = a;
-    return APMOE_OK;
-}
-
-extern "C" void apmoe_arena_destroy(apmoe_arena* a) { delete a; }
-
-extern "C" int apmoe_arena_alloc(apmoe_arena* a, uint64_t bytes, uint64_t* off) {
-    if (!a || !off || bytes == 0) return APMOE_EINVAL;
-    return a->alloc(bytes, off) ? APMOE_OK : APMOE_ENOSPACE;
-}
-
-extern "C" int apmoe_arena_take(apmoe_arena* a, uint64_t off, uint64_t bytes) {
-    if (!a || off % kAlign) return APMOE_EINVAL;
-    return a->take(off, bytes) ? APMOE_OK : APMOE_ENOSPACE;
-}
-
-extern "C" int apmoe_arena_release(apmoe_arena* a, uint64_t off, uint64_t bytes) {
-    if (!a) return APMOE_EINVAL;
-    return a->release(off, bytes) ? APMOE_OK : APMOE_EINVAL;
-}
-
-extern "C" int apmoe_arena_stats(const apmoe_arena* a, uint64_t* free_bytes, uint64_t* largest, int* n_ranges) {
-    if (!a) return APMOE_EINVAL;
-    a->stats(free_bytes, largest, n_ranges);
-    return APMOE_OK;
-}
 
 // ---------------------------------------------------------------------------
 // Pager
@@ -157,21 +39,10 @@ extern "C" int apmoe_arena_stats(const apmoe_arena* a, uint64_t* free_bytes, uin
 namespace apmoe {
 namespace {
 
-struct Block {
-    uint64_t off = 0, len = 0;   // len 0: nothing held
-};
-
-struct PagedMat {
-    uint64_t slab = 0;            // bytes of one packed plane slab
-    uint64_t lut_bytes[4] = {};   // bytes of the b-bit LUT, b = 3..6
+struct PagedMat : MatResidency {
     const char* host_planes = nullptr;
     const char* host_lut[4] = {};
     uint64_t* desc = nullptr;     // device address of this matrix's apmoe_mat
-    Block planes, lut;            // resident now
-    int have = 0, lut_b = 0;      // resident plane count; bitwidth of the resident LUT (0: none)
-    Block planes_new, lut_new;    // after the staged change
-    int want = 0;
-    bool grown = false, moved = false, new_lut = false;   // what the staged change claimed
 };
 
 struct Patch {
@@ -211,6 +82,7 @@ struct apmoe_pager {
     hipEvent_t last_commit = nullptr;
     bool committed_once = false;
     char* host_buf = nullptr;        // pinned staging of the commit's patch list
+    uint64_t n_copies = 0;           // ranges the last stage copied
     uint64_t dev_buf = 0;            // its device copy, carved from the arena
     size_t buf_bytes = 0;
     struct Pending {
@@ -240,56 +112,12 @@ struct apmoe_pager {
 namespace apmoe {
 namespace {
 
-// Undo the claims of a stage that failed before any copy was enqueued.
 void unstage(apmoe_pager* pg) {
-    for (PagedMat& m : pg->mats) {
-        if (m.moved) pg->arena.release(m.planes_new.off, m.planes_new.len);
-        if (m.grown) pg->arena.release(m.planes.off + m.planes.len, m.planes_new.len - m.planes.len);
-        if (m.new_lut) pg->arena.release(m.lut_new.off, m.lut_new.len);
-        m.planes_new = m.planes;
-        m.lut_new = m.lut;
-        m.want = m.have;
-        m.grown = m.moved = m.new_lut = false;
-    }
+    unstage(pg->arena, pg->mats);
     pg->retire_next.clear();
 }
 
-// Claim the blocks every matrix needs after the change; false when the arena
-// cannot hold them (the claims made so far are flagged for unstage).
-bool claim(apmoe_pager* pg) {
-    for (PagedMat& m : pg->mats) {
-        m.planes_new = m.planes;
-        m.lut_new = m.lut;
-        m.grown = m.moved = m.new_lut = false;
-    }
-    for (PagedMat& m : pg->mats) {
-        const uint64_t need = (uint64_t)m.want * m.slab;   // slab is a multiple of 256 bytes
-        if (m.want > m.have) {
-            // grow in place when the bytes after the block are free, else a new block
-            if (m.have && pg->arena.take(m.planes.off + m.planes.len, need - m.planes.len)) {
-                m.planes_new = Block{m.planes.off, need};
-                m.grown = true;
-            } else {
-                uint64_t off;
-                if (!pg->arena.alloc(need, &off)) return false;
-                m.planes_new = Block{off, need};
-                m.moved = true;
-            }
-        } else if (m.want < m.have) {
-            m.planes_new = m.want ? Block{m.planes.off, need} : Block{};
-        }
-        if (m.want != m.lut_b) {
-            m.lut_new = Block{};
-            if (m.want) {
-                uint64_t off;
-                if (!pg->arena.alloc(m.lut_bytes[m.want - 3], &off)) return false;
-                m.lut_new = Block{off, align_up(m.lut_bytes[m.want - 3])};
-                m.new_lut = true;
-            }
-        }
-    }
-    return true;
-}
+bool claim(apmoe_pager* pg) { return claim(pg->arena, pg->mats); }
 
 }  // namespace
 }  // namespace apmoe
@@ -370,36 +198,29 @@ extern "C" int apmoe_pager_stage(apmoe_pager* pg, const int8_t* bits_new, void* 
             return APMOE_ENOSPACE;
         }
     }
-    // enqueue the copies; record what the commit retires
+    // enqueue the copies (device-to-device moves of blocks that cannot grow in
+    // place, host-to-device planes and LUTs); record what the commit retires
     hipStream_t cs = as_stream(copy_stream);
     pg->h2d_bytes = pg->d2d_bytes = 0;
+    pg->n_copies = 0;
     pg->retire_next.clear();
     bool ok = true;
+    auto copy = [&](char* d, const char* s_, uint64_t n, hipMemcpyKind kind) {
+        ok = ok && hipMemcpyAsync(d, s_, n, kind, cs) == hipSuccess;
+        (kind == hipMemcpyHostToDevice ? pg->h2d_bytes : pg->d2d_bytes) += n;
+        ++pg->n_copies;
+    };
     for (PagedMat& m : pg->mats) {
         if (m.want > m.have) {
-            char* dst = pg->base + m.planes_new.off;
-            if (m.moved && m.have) {
-                const uint64_t n = (uint64_t)m.have * m.slab;
-                ok = ok && hipMemcpyAsync(dst, pg->base + m.planes.off, n, hipMemcpyDeviceToDevice, cs) == hipSuccess;
-                pg->d2d_bytes += n;
-            }
-            const uint64_t o = (uint64_t)m.have * m.slab, n = (uint64_t)(m.want - m.have) * m.slab;
-            ok = ok && hipMemcpyAsync(dst + o, m.host_planes + o, n, hipMemcpyHostToDevice, cs) == hipSuccess;
-            pg->h2d_bytes += n;
-            if (m.moved && m.planes.len) pg->retire_next.push_back(m.planes);
-        } else if (m.want < m.have) {
-            pg->retire_next.push_back(Block{m.planes.off + m.planes_new.len, m.planes.len - m.planes_new.len});
+            char* d = pg->base + m.planes_new.off;
+            if (m.moved && m.have) copy(d, pg->base + m.planes.off, (uint64_t)m.have * m.slab, hipMemcpyDeviceToDevice);
+            const uint64_t o = (uint64_t)m.have * m.slab;
+            copy(d + o, m.host_planes + o, (uint64_t)(m.want - m.have) * m.slab, hipMemcpyHostToDevice);
         }
-        if (m.want != m.lut_b) {
-            if (m.new_lut) {
-                const uint64_t n = m.lut_bytes[m.want - 3];
-                ok = ok && hipMemcpyAsync(pg->base + m.lut_new.off, m.host_lut[m.want - 3], n, hipMemcpyHostToDevice,
-                                          cs) == hipSuccess;
-                pg->h2d_bytes += n;
-            }
-            if (m.lut.len) pg->retire_next.push_back(m.lut);
-        }
+        if (m.want != m.lut_b && m.new_lut)
+            copy(pg->base + m.lut_new.off, m.host_lut[m.want - 3], m.lut_bytes[m.want - 3], hipMemcpyHostToDevice);
     }
+    pg->retire_next = retired_blocks(pg->mats);
     if (ok) ok = hipEventRecord(pg->copies_done, cs) == hipSuccess;
     if (!ok) {
         (void)hipStreamSynchronize(cs);   // no copy may still land in a block unstage returns
@@ -448,19 +269,15 @@ extern "C" int apmoe_pager_commit(apmoe_pager* pg, void* stream) {
         p.blocks.swap(pg->retire_next);
         pg->pending.push_back(std::move(p));
     }
-    for (PagedMat& m : pg->mats) {
-        m.planes = m.planes_new;
-        m.lut = m.lut_new;
-        m.have = m.want;
-        m.lut_b = m.want;
-    }
+    adopt(pg->mats);
     pg->bits_now = pg->bits_staged;
     pg->staged = false;
     return APMOE_OK;
 }
 
 extern "C" int apmoe_pager_stats(apmoe_pager* pg, uint64_t* resident_bytes, uint64_t* free_bytes,
-                                 uint64_t* largest_free, uint64_t* h2d_bytes, uint64_t* d2d_bytes) {
+                                 uint64_t* largest_free, uint64_t* h2d_bytes, uint64_t* d2d_bytes,
+                                 uint64_t* copy_ranges) {
     if (!pg) return APMOE_EINVAL;
     pg->reap(false);
     uint64_t r = 0;
@@ -469,6 +286,7 @@ extern "C" int apmoe_pager_stats(apmoe_pager* pg, uint64_t* resident_bytes, uint
     pg->arena.stats(free_bytes, largest_free, nullptr);
     if (h2d_bytes) *h2d_bytes = pg->h2d_bytes;
     if (d2d_bytes) *d2d_bytes = pg->d2d_bytes;
+    if (copy_ranges) *copy_ranges = pg->n_copies;
     return APMOE_OK;
 }
 

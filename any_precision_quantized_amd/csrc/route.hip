@@ -32,7 +32,8 @@ template <int kTB>
 __global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* __restrict__ x, int T, int H,
                                                                   const float* __restrict__ w_router,
                                                                   const float* __restrict__ bias, float scale,
-                                                                  int E, double* __restrict__ L) {
+                                                                  int E, double* __restrict__ L,
+                                                                  float* __restrict__ norms) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int t0 = blockIdx.x * kTB;
@@ -46,10 +47,14 @@ __global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* _
     for (int j = 0; j < kEPW; ++j) wr[j] = w_router + (size_t)min(e0 + j, E - 1) * H;
 
     double acc[kTB][kEPW];
+    float sq[kTB];   // ||x_t||^2 on the first expert tile's first wave (the same order as norms_kernel)
+    const bool do_norm = norms && blockIdx.y == 0 && wave == 0;
 #pragma unroll
-    for (int t = 0; t < kTB; ++t)
+    for (int t = 0; t < kTB; ++t) {
+        sq[t] = 0.f;
 #pragma unroll
         for (int j = 0; j < kEPW; ++j) acc[t][j] = 0.0;
+    }
 #pragma unroll 2
     for (int h = 4 * lane; h < H; h += 4 * kWave) {   // H % 32 == 0: h + 3 < H
         float4v_t wv[kEPW];
@@ -62,8 +67,17 @@ __global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* _
             for (int j = 0; j < kEPW; ++j)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc[t][j] = fma((double)xv[c], (double)wv[j][c], acc[t][j]);
+            if (do_norm)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sq[t] = fmaf((float)xv[c], (float)xv[c], sq[t]);
         }
     }
+    if (do_norm)
+#pragma unroll
+        for (int t = 0; t < kTB; ++t) {
+            const float n2 = wave_sum(sq[t]);
+            if (lane == 0 && t0 + t < T) norms[t0 + t] = sqrtf(n2);
+        }
 #pragma unroll
     for (int t = 0; t < kTB; ++t)
 #pragma unroll
@@ -123,8 +137,9 @@ __global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __
                                                                  const float* __restrict__ w_router,
                                                                  const float* __restrict__ bias, float scale, int E,
                                                                  int k, int32_t* __restrict__ topk_ids,
-                                                                 float* __restrict__ topk_w) {
+                                                                 float* __restrict__ topk_w, float* __restrict__ norms) {
     constexpr int EC = 8;   // TB * EC <= 16 fp64 accumulators
+    __shared__ float sqq[4][TB];   // ||x_t||^2 per hidden quarter
     extern __shared__ double dyn[];
     double* P = dyn;                                      // [4][TB][E]
     double* chosen = dyn + 4 * TB * E;                    // [kFWaves][k]
@@ -136,7 +151,14 @@ __global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __
     const half_t* xr[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) xr[t] = x + (size_t)min(t0 + t, T - 1) * H;   // rows past T: a valid row, never used
+    // the four quarter waves of expert group 0 also sum x^2 (token norms) over
+    // the x values they load for their first expert chunk
+    const bool do_norm = norms && eg == 0;
     for (int e0 = eg * EC; e0 < E; e0 += 4 * EC) {
+        const bool nrm = do_norm && e0 == 0;
+        float sq[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) sq[t] = 0.f;
         const float* wr[EC];
 #pragma unroll
         for (int j = 0; j < EC; ++j) wr[j] = w_router + (size_t)min(e0 + j, E - 1) * H;
@@ -156,6 +178,9 @@ __global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __
                 for (int j = 0; j < EC; ++j)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) acc[t][j] = fma((double)xv[c], (double)wv[j][c], acc[t][j]);
+                if (nrm)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) sq[t] = fmaf((float)xv[c], (float)xv[c], sq[t]);
             }
         }
 #pragma unroll
@@ -166,8 +191,18 @@ __global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __
                 const int e = e0 + j;
                 if (lane == 0 && e < E) P[(hq * TB + t) * E + e] = sm;
             }
+        if (nrm)
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const float s2 = wave_sum(sq[t]);
+                if (lane == 0) sqq[hq][t] = s2;
+            }
     }
     __syncthreads();
+    if (norms && threadIdx.x < TB && t0 + (int)threadIdx.x < T) {
+        const int t = threadIdx.x;
+        norms[t0 + t] = sqrtf((sqq[0][t] + sqq[1][t]) + (sqq[2][t] + sqq[3][t]));
+    }
     for (int i = threadIdx.x; i < TB * E; i += blockDim.x) {
         const int e = i % E;
         const double sm = (P[i] + P[TB * E + i]) + (P[2 * TB * E + i] + P[3 * TB * E + i]);
@@ -305,8 +340,8 @@ size_t route_workspace_bytes(int T, int E, int H) {
 using namespace apmoe;
 
 extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const float* bias,
-                           float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, float* x_norms,
+                           void* ws, size_t ws_bytes, void* stream) {
     if (T < 0 || H <= 0 || H % 32 || E < 1 || E > APMOE_MAX_EXPERTS || k < 1 || k > E) return APMOE_EINVAL;
     if (!(logit_scale > 0.0f)) return APMOE_EINVAL;
     if (T == 0) return APMOE_OK;
@@ -318,7 +353,7 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
     case TB_:                                                                                                 \
         hipLaunchKernelGGL(route_kernel<TB_>, dim3((T + TB_ - 1) / TB_), dim3(kFWaves * kWave),                \
                            (4 * TB_ * E + kFWaves * k) * sizeof(double), s, xh, T, H, w_router, bias, logit_scale, \
-                           E, k, topk_ids, topk_w);                                                           \
+                           E, k, topk_ids, topk_w, x_norms);                                                  \
         return launch_status();
         APMOE_ROUTE_FUSED(1)
 #undef APMOE_ROUTE_FUSED
@@ -335,13 +370,13 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
     const dim3 grid((T + tb - 1) / tb, etiles);
     if (tb == 4)
         hipLaunchKernelGGL(logits_kernel<4>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
-                           E, L);
+                           E, L, x_norms);
     else if (tb == 2)
         hipLaunchKernelGGL(logits_kernel<2>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
-                           E, L);
+                           E, L, x_norms);
     else
         hipLaunchKernelGGL(logits_kernel<1>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
-                           E, L);
+                           E, L, x_norms);
     int rc = launch_status();
     if (rc != APMOE_OK) return rc;
     hipLaunchKernelGGL(select_kernel, dim3((T + kSelWaves - 1) / kSelWaves), dim3(kSelWaves * kWave), 0, s, L, T, E,

@@ -25,8 +25,12 @@ from . import _lib
 MATS = ("gate", "up", "down")
 DESC_WORDS = 18          # 3 matrices x (planes, lut[4], w16) pointers
 # Groups of at least this many slots take the dequantise-to-LDS + MFMA tile path;
-# smaller ones take the bit-plane GEMV path (one pass over K covers 64 tokens).
-DEFAULT_MFMA_MIN_TOKENS = 65   # a group of up to 64 slots is one GEMV pass
+# smaller ones take the bit-plane GEMV path (one pass over K covers 64 tokens,
+# a larger group takes several).  Measured on the Mixtral-shaped layer (8
+# experts, top-2): groups of 52-76 slots run 1.8x faster on the GEMV path,
+# groups of 114-158 equally fast on both, groups of 226-293 1.3x faster as
+# tiles, so the crossover sits at about 160.
+DEFAULT_MFMA_MIN_TOKENS = 160
 
 
 class ExpertTable:
@@ -174,10 +178,12 @@ class MoELayer:
         self.out = torch.empty((T, H), dtype=torch.float16, **dev)
         nws = _lib.workspace_bytes(T, kk, E2, H, I)
         self.ws = torch.empty(nws, dtype=torch.uint8, **dev) if nws else None
-        # routing statistics for the planner (per routed expert) and their token norms
-        self.mass = torch.empty(E, dtype=torch.float32, **dev)
-        self.wnorm = torch.empty(E, dtype=torch.float32, **dev)
-        self.ws_stats = torch.empty(max(4 * T, 4), dtype=torch.uint8, **dev)
+        # routing statistics for the planner (per routed expert), computed in
+        # every forward by the router (token norms) and the grouping (sums)
+        self.mass = torch.zeros(E, dtype=torch.float32, **dev)
+        self.wnorm = torch.zeros(E, dtype=torch.float32, **dev)
+        self.x_norms = torch.zeros(max(T, 1), dtype=torch.float32, **dev)
+        self.ws_stats = torch.empty(max(8 * S, 4 * T, 4), dtype=torch.uint8, **dev)
         if shared is not None and not n:
             # the shared expert runs on a side stream (default priority) with
             # its own workspace, overlapping routing and the routed experts
@@ -211,19 +217,22 @@ class MoELayer:
         _lib.commit_bits(bits, self.bits[self.n_shared:])
         return _lib.OK
 
-    def route_stats(self, x):
+    def route_stats(self, x=None):
         """Routing mass and routing-weighted input norm of every routed expert
-        over the last forward's routing (x: the input it routed), fp32 [E]
-        device tensors (reused by later calls)."""
-        _lib.route_stats(x, self.topk_ids, self.topk_w, self.E, self.mass, self.wnorm, self.ws_stats)
+        over the last forward's routing, fp32 [E] device tensors (reused by
+        later calls).  The forward computes them in its router and grouping
+        launches; given x, they are recomputed with apmoe_route_stats instead
+        (two launches of their own)."""
+        if x is not None:
+            _lib.route_stats(x, self.topk_ids, self.topk_w, self.E, self.mass, self.wnorm, self.ws_stats)
         return self.mass, self.wnorm
 
     def replan(self, x, levels, harm, nbytes, floor_bits, budget):
         """Re-plan the routed experts' bitwidths from the offline harm table
-        corrected by this step's routing statistics (apmoe_plan_routed), commit
-        the plan in stream order and return (status, bits).  Synchronises to
-        read the statistics back."""
-        mass, wnorm = self.route_stats(x)
+        corrected by the last forward's routing statistics (apmoe_plan_routed),
+        commit the plan in stream order and return (status, bits).
+        Synchronises to read the statistics back."""
+        mass, wnorm = self.route_stats()
         status, bits = _lib.plan_routed(levels, harm, nbytes, floor_bits, budget, mass.cpu().numpy(),
                                         wnorm.cpu().numpy())
         if status == _lib.OK:
@@ -254,8 +263,10 @@ class MoELayer:
             ysh = self.Y_sh
         table = self._fused(ex, sh) if n else ex
         E2, kk = self.E2, self.kk
-        _lib.route(x, self.w_router, self.bias, self.logit_scale, k, self.topk_ids, self.topk_w, self.ws)
-        _lib.permute(self.topk_ids, E, self.counts, self.offsets, self.sorted_slots, self.pos_of_slot, n)
+        _lib.route(x, self.w_router, self.bias, self.logit_scale, k, self.topk_ids, self.topk_w, self.ws,
+                   x_norms=self.x_norms)
+        _lib.permute(self.topk_ids, E, self.counts, self.offsets, self.sorted_slots, self.pos_of_slot, n,
+                     stats=(self.topk_w, self.x_norms, self.mass, self.wnorm, self.ws_stats))
         _lib.bitplane_lut_gemm(_lib.GATE_UP_SWIGLU, table.desc, self.bits, E2, self.offsets, self.sorted_slots,
                                kk, x, self.A, T, H, I, self.mfma_min_tokens, self.ws)
         _lib.bitplane_lut_gemm(_lib.DOWN, table.desc, self.bits, E2, self.offsets, self.sorted_slots,

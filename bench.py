@@ -153,13 +153,16 @@ def counted_traffic(kernel, workload):
 def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     """Throughput while a re-plan's plane copies run (plane paging).
 
-    A second layer runs on paged weights (PagedExperts).  Each repetition
-    demotes every bit-plane expert above 3 bits by one bit (committed, so only
-    the lower LUTs move), then enqueues `steps` layer steps, stages the
-    promotion back to `bits` (host-to-device plane and LUT copies on the copy
-    stream, issued while those steps run), enqueues `steps` more and commits.
-    Per-step events give the steps that overlapped the copy window; their
-    mean time against an idle run's is the loss."""
+    A second layer runs on paged weights (PagedExperts), its step captured as
+    a HIP graph.  Each repetition demotes every bit-plane expert above 3 bits
+    by one bit (committed, so only the lower LUTs move), enqueues `steps`
+    graph replays, stages the promotion back to `bits` (the plane and LUT
+    copies go out on the copy stream while those replays run; the host only
+    issues them), enqueues `steps` more replays and commits.  The host stays
+    far ahead of the GPU (a replay costs it microseconds, the GPU a whole
+    step), so the queue never drains: every step interval comes from GPU
+    events.  The steps whose interval overlaps the copy window, against the
+    mean of an idle run, give the loss."""
     import numpy as np
     import torch
     from any_precision_quantized_amd import _lib
@@ -174,57 +177,61 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
     stream = torch.cuda.current_stream()
     low = np.where((bits > 3) & (bits <= 6), bits - 1, bits).astype(np.int8)
+    graph = lay.graph(x)
 
-    def start():
+    def event():
         e = torch.cuda.Event(enable_timing=True)
         e.record(stream)
-        return [e]
+        return e
 
     def enqueue(n, evs):
         for _ in range(n):
-            lay.forward(x)
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(stream)
-            evs.append(e)
+            graph.replay()
+            evs.append(event())
 
     def step_us(evs):
         return [a.elapsed_time(b) * 1e3 for a, b in zip(evs[:-1], evs[1:])]
 
     for _ in range(10):
-        lay.forward(x)
+        graph.replay()
     torch.cuda.synchronize()
-    evs = start()
+    evs = [event()]
     enqueue(2 * steps, evs)
     torch.cuda.synchronize()
     idle = step_us(evs)
-    during, copy_ms, h2d, d2d = [], [], 0, 0
+    during, copy_ms, stage_us, h2d, d2d, ranges = [], [], [], 0, 0, 0
     for _ in range(reps):
         if pe.apply(low) != _lib.OK:
             raise RuntimeError("paging probe: demotion did not fit")
         torch.cuda.synchronize()
-        evs = start()
+        evs = [event()]
         enqueue(steps, evs)
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(pe.copy_stream)
+        t0 = time.perf_counter()
         if pe.stage(bits) != _lib.OK:
             raise RuntimeError("paging probe: promotion did not fit")
+        stage_us.append((time.perf_counter() - t0) * 1e6)
         c1.record(pe.copy_stream)
         enqueue(steps, evs)
         pe.commit(bits)
         torch.cuda.synchronize()
         st = pe.stats()
-        h2d, d2d = st["h2d"], st["d2d"]
+        h2d, d2d, ranges = st["h2d"], st["d2d"], st["ranges"]
         lo, hi = evs[0].elapsed_time(c0), evs[0].elapsed_time(c1)
         copy_ms.append(hi - lo)
         for i, us in enumerate(step_us(evs)):
             a, b = evs[0].elapsed_time(evs[i]), evs[0].elapsed_time(evs[i + 1])
             if b > lo and a < hi:
                 during.append(us)
+    del graph
     pe.close()
     idle_us = float(np.mean(idle))
     during_us = float(np.mean(during)) if during else None
     cm = float(np.mean(copy_ms))
     return {"replan": "every bit-plane expert above 3 bits promoted by one plane (b-1 -> b) while the layer runs",
+            "copy_ranges": int(ranges),
+            "stage_host_us": round(float(np.median(stage_us)), 1),
             "h2d_bytes": int(h2d), "d2d_bytes": int(d2d), "copy_ms": round(cm, 3),
             "h2d_GBps": round(h2d / (cm * 1e-3) / 1e9, 2) if cm > 0 else None,
             "step_us_idle": round(idle_us, 2),
@@ -289,65 +296,17 @@ def codec_probe(inp, reps=5):
             "decode_hbm_frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen_decode")
-    ap.add_argument("--mfma-min-tokens", type=int, default=None)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-paging-probe", action="store_true",
-                    help="skip the throughput-under-plane-paging probe")
-    ap.add_argument("--no-codec-probe", action="store_true",
-                    help="skip the exponent-codec decode probe")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time eager launches only (no HIP graph replay of the step)")
-    ap.add_argument("--serial-shared", action="store_true",
-                    help="run the shared expert on the main stream instead of the side stream")
-    ap.add_argument("--replica-bytes", type=float, default=1.0e9,
-                    help="weight bytes the rotating replicas must span (MALL defeat)")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only copy MIB MiB device to device five times (scale for HBM byte counters)")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this layer runs on one GPU; --gpus must be 1 (no multi-GPU path is built)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
+    """Time `steps` whole layer steps of one workload (HIP graph replays over
+    rotating weight replicas) and, in a separate pass, every launch of a step
+    with events on its stream.  Returns the bench fields of that workload."""
     import numpy as np
     import torch
 
-    import synth
     from any_precision_quantized_amd import _lib
     from any_precision_quantized_amd import layer as L
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
-        return
-    cfg = synth.get(args.workload)
     mfma_min = args.mfma_min_tokens or L.DEFAULT_MFMA_MIN_TOKENS
-    inp = synth.make_inputs(cfg, seed=0)
-    if inp.bits is None:
-        pl = inp.plan
-        st, bits = _lib.plan_bitwidths(pl["levels"], pl["harm"], pl["bytes"], pl["floors"], pl["budget"])
-        if st != _lib.OK:
-            raise RuntimeError(f"planner: {_lib.strerror(st)}")
-    else:
-        bits = np.asarray(inp.bits, dtype=np.int8)
-
     layer = L.from_inputs(inp, bits=bits, mfma_min_tokens=mfma_min)
     x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
     layer.forward(x)
@@ -396,9 +355,12 @@ def main():
             seq.append(("side_done", None, None))
         seq += [
             ("route", lambda: lib.apmoe_route(p(x), T, H, p(layer.w_router), p(layer.bias), layer.logit_scale,
-                                              E, k, p(layer.topk_ids), p(layer.topk_w), ws, wsb, sp), stream),
+                                              E, k, p(layer.topk_ids), p(layer.topk_w), p(layer.x_norms), ws, wsb,
+                                              sp), stream),
             ("permute", lambda: lib.apmoe_permute(p(layer.topk_ids), T, k, E, nsh, p(layer.counts), p(layer.offsets),
-                                                  p(layer.sorted_slots), p(layer.pos_of_slot), None, 0, sp), stream),
+                                                  p(layer.sorted_slots), p(layer.pos_of_slot), p(layer.topk_w),
+                                                  p(layer.x_norms), p(layer.mass), p(layer.wnorm), p(layer.ws_stats),
+                                                  layer.ws_stats.numel(), sp), stream),
         ]
         for stage, name, src, dst in ((_lib.GATE_UP_SWIGLU, "gate_up", x, layer.A),
                                       (_lib.DOWN, "down", layer.A, layer.Y)):
@@ -415,8 +377,8 @@ def main():
                                                           nsh, H, ysh, p(layer.out), sp), stream))
         return seq
 
-    steps = [launches(r) for r in range(R)]
-    names = [n for n, fn, _ in steps[0] if fn is not None]
+    seqs = [launches(r) for r in range(R)]
+    names = [n for n, fn, _ in seqs[0] if fn is not None]
 
     def run(seq, timed_name=None, ev=None):
         for n, fn, st in seq:
@@ -441,59 +403,60 @@ def main():
 
     # Per-launch durations (separate pass) to find the dominant kernel.
     per = {n: 0.0 for n in names}
-    probe_steps = max(5, min(50, args.steps))
-    for i in range(args.warmup):
-        run(steps[i % R])
+    for i in range(warmup):
+        run(seqs[i % R])
     torch.cuda.synchronize()
     for name in names:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(probe_steps)]
         for i in range(probe_steps):
-            run(steps[i % R], name, evs[i])
+            run(seqs[i % R], name, evs[i])
         torch.cuda.synchronize()
         per[name] = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3   # us
     dominant = max(names, key=lambda n: per[n])
-    # routing statistics for the planner (outside the layer step: the planner
-    # reads them at a step boundary), timed the same way
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(probe_steps)]
-    for i in range(probe_steps):
-        evs[i][0].record(stream)
-        rc = lib.apmoe_route_stats(p(x), T, H, p(layer.topk_ids), p(layer.topk_w), k, E, p(layer.mass),
-                                   p(layer.wnorm), p(layer.ws_stats), layer.ws_stats.numel(), sp)
-        evs[i][1].record(stream)
-        if rc != 0:
-            raise _lib.ApmoeError(rc, "route_stats")
-    torch.cuda.synchronize()
-    route_stats_us = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3
+    route_stats_us = None
+    if time_stats:
+        # routing statistics for the planner (outside the layer step: the planner
+        # reads them at a step boundary), timed the same way
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(probe_steps)]
+        for i in range(probe_steps):
+            evs[i][0].record(stream)
+            rc = lib.apmoe_route_stats(p(x), T, H, p(layer.topk_ids), p(layer.topk_w), k, E, p(layer.mass),
+                                       p(layer.wnorm), p(layer.ws_stats), layer.ws_stats.numel(), sp)
+            evs[i][1].record(stream)
+            if rc != 0:
+                raise _lib.ApmoeError(rc, "route_stats")
+        torch.cuda.synchronize()
+        route_stats_us = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3
 
     # Timed region: K whole steps; the dominant launch is bracketed by events.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.warmup):
-        run(steps[i % R])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(warmup):
+        run(seqs[i % R])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(steps[i % R], dominant, evs[i])
+    for i in range(steps):
+        run(seqs[i % R], dominant, evs[i])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    dom_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
+    dom_us = sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3
 
-    ms_eager = dt / args.steps * 1e3
+    ms_eager = dt / steps * 1e3
     # The same K steps replayed as HIP graphs (one per weight replica): what a
     # serving loop that captures the layer pays, without per-launch host work.
     use_graph = not args.no_graph and side is None
     if use_graph:
         graphs = [layer.graph(x, tables[r], shared[r]) for r in range(R)]
-        for i in range(args.warmup):
+        for i in range(warmup):
             graphs[i % R].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             graphs[i % R].replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         del graphs
-    ms_per_step = dt / args.steps * 1e3
-    tokens_per_s = T * args.steps / dt
+    ms_per_step = dt / steps * 1e3
+    tokens_per_s = T * steps / dt
     layer_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     dom_bytes = by.get(dominant, 0)
     if dominant.endswith("_tile"):
@@ -514,8 +477,8 @@ def main():
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -534,11 +497,131 @@ def main():
         "expert_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "roofline": roofline,
         "per_launch_us": {n: round(per[n], 2) for n in names},
-        "route_stats_us": round(route_stats_us, 2),
+        "route_stats_us": None if route_stats_us is None else round(route_stats_us, 2),
         "per_launch_bytes": {n: int(by.get(n, 0)) for n in names},
     }
+    gu, dn = per.get("gate_up_gemv"), per.get("down_gemv")
+    if gu and dn and by["gate_up_gemv"] + by["down_gemv"] > 0:   # the two GEMV stages together against HBM peak
+        gb = (by["gate_up_gemv"] + by["down_gemv"]) / ((gu + dn) * 1e-6) / 1e9
+        result["gemv_stages"] = {"algorithmic_bytes": int(by["gate_up_gemv"] + by["down_gemv"]),
+                                 "us": round(gu + dn, 2), "GBps": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4)}
+    return result
+
+
+def planned_bits(inp):
+    """Bitwidths of a generated layer: fixed by the workload, or from the host planner."""
+    import numpy as np
+    from any_precision_quantized_amd import _lib
+    if inp.bits is not None:
+        return np.asarray(inp.bits, dtype=np.int8)
+    pl = inp.plan
+    st, bits = _lib.plan_bitwidths(pl["levels"], pl["harm"], pl["bytes"], pl["floors"], pl["budget"])
+    if st != _lib.OK:
+        raise RuntimeError(f"planner: {_lib.strerror(st)}")
+    return bits
+
+
+WORKLOADS = ["tiny", "qwen_decode", "mixtral_decode_t1", "mixtral_decode_t8", "mixtral_decode_t32", "e128_decode",
+             "mixtral_prefill"]
+
+
+def other_workloads(args, primary):
+    """A compact line for every other workload of the layer: whole-step time
+    and tokens/s (graph replays), the dominant launch against its roofline,
+    and the two GEMV stages together against HBM peak.  The Mixtral-shaped
+    decode batches share one draw of weights (they differ only in tokens)."""
+    import dataclasses
+    import gc
+
+    import torch
+
+    import synth
+    out = {}
+    mixtral = None
+    for name in WORKLOADS:
+        if name == primary:
+            continue
+        cfg = synth.get(name)
+        if name.startswith("mixtral_decode_t"):
+            if mixtral is None:
+                mixtral = synth.make_inputs(synth.get("mixtral_decode_t32"), seed=0)
+            inp = dataclasses.replace(mixtral, cfg=cfg, x=mixtral.x[: cfg.T])
+        else:
+            inp = synth.make_inputs(cfg, seed=0)
+        prefill = cfg.T > 1024
+        steps, warmup, probe = (args.workload_steps // 5, 3, 5) if prefill else (args.workload_steps, 10, 20)
+        r = measure(args, cfg, inp, planned_bits(inp), steps, warmup, probe, time_stats=False)
+        rf = r["roofline"]
+        out[name] = {"workload": r["config"]["workload"], "ms_per_step": round(r["ms_per_step"], 4),
+                     "tokens_per_s": round(r["value"], 1), "steps": steps,
+                     "dominant": {k: rf[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "avg_us")},
+                     "gemv_stages": r.get("gemv_stages"), "per_launch_us": r["per_launch_us"]}
+        del inp
+        gc.collect()
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen_decode")
+    ap.add_argument("--mfma-min-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paging-probe", action="store_true",
+                    help="skip the throughput-under-plane-paging probe")
+    ap.add_argument("--no-codec-probe", action="store_true",
+                    help="skip the exponent-codec decode probe")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no HIP graph replay of the step)")
+    ap.add_argument("--serial-shared", action="store_true",
+                    help="run the shared expert on the main stream instead of the side stream")
+    ap.add_argument("--replica-bytes", type=float, default=1.0e9,
+                    help="weight bytes the rotating replicas must span (MALL defeat)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="measure only --workload (no compact line per other workload)")
+    ap.add_argument("--workload-steps", type=int, default=50,
+                    help="timed steps per other workload (a fifth of it for the prefill)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device five times (scale for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this layer runs on one GPU; --gpus must be 1 (no multi-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from any_precision_quantized_amd import _lib
+    from any_precision_quantized_amd import layer as L
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return
+    cfg = synth.get(args.workload)
+    inp = synth.make_inputs(cfg, seed=0)
+    bits = planned_bits(inp)
+    result = measure(args, cfg, inp, bits, args.steps, args.warmup, max(5, min(50, args.steps)))
+    mfma_min = args.mfma_min_tokens or L.DEFAULT_MFMA_MIN_TOKENS
+    if not args.no_workloads:
+        result["workloads"] = other_workloads(args, cfg.name)
     if not args.no_paging_probe:
-        del tables, shared, steps
         result["paging"] = paging_probe(cfg, inp, bits, mfma_min)
     if not args.no_codec_probe:
         result["exp_codec"] = codec_probe(inp)

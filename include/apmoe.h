@@ -101,6 +101,9 @@ typedef struct apmoe_expert {
  *  x        fp16 [T][H]          w_router fp32 [E][H]
  *  bias     fp32 [E] or NULL     logit_scale > 0
  *  topk_ids int32 [T][k] (out)   topk_w   fp32 [T][k] (out)
+ *  x_norms  fp32 [T] (out) or NULL: ||x_t||_2 (squares summed in fp32 in a
+ *           fixed order), computed from the x rows the router already reads;
+ *           apmoe_permute turns them into the planner's routing statistics.
  *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I)
  *           bytes.  Small problems (a token group's share of T * E * H
  *           multiply-adds fits one workgroup) keep the logits on chip and
@@ -109,8 +112,8 @@ typedef struct apmoe_expert {
  * Needs 1 <= k <= E <= APMOE_MAX_EXPERTS, H > 0 and H % 32 == 0.
  */
 int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const float* bias,
-                float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, void* ws,
-                size_t ws_bytes, void* stream);
+                float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, float* x_norms,
+                void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Routing statistics for the bitwidth planner, over the slots of one
@@ -147,12 +150,18 @@ int apmoe_route_stats(const uint16_t* x, int T, int H, const int32_t* topk_ids, 
  *  sorted_slots[p] slot at sorted position p                      int32 [S]
  *  pos_of_slot[s]  sorted position of slot s (inverse)            int32 [S]
  * Every topk_ids entry must lie in [0, E); E2 <= APMOE_MAX_EXPERTS.
- * ws/ws_bytes: unused (pass NULL, 0); kept so the call can grow a workspace
- * without an ABI change.
+ * Routing statistics in the same launch (optional; the same sums as
+ * apmoe_route_stats, for the E routed experts): with mass != NULL, also
+ *  mass[e]  = sum of topk_w over the slots routed to e              fp32 [E]
+ *  wnorm[e] = sum of topk_w * x_norms[t] over the same slots        fp32 [E]
+ * summed in a fixed order from topk_w fp32 [T][k] and x_norms fp32 [T] (as
+ * apmoe_route wrote them); ws/ws_bytes must then hold S * 8 bytes
+ * (APMOE_ENOSPACE otherwise).  With mass == NULL, topk_w, x_norms, wnorm and
+ * ws are ignored (pass NULL, 0).
  */
 int apmoe_permute(const int32_t* topk_ids, int T, int k, int E, int n_shared, int32_t* counts,
-                  int32_t* offsets, int32_t* sorted_slots, int32_t* pos_of_slot, void* ws,
-                  size_t ws_bytes, void* stream);
+                  int32_t* offsets, int32_t* sorted_slots, int32_t* pos_of_slot, const float* topk_w,
+                  const float* x_norms, float* mass, float* wnorm, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * One stage of every routed expert's FFN over its group of slots, reading each
@@ -370,7 +379,8 @@ int apmoe_arena_stats(const apmoe_arena* arena, uint64_t* free_bytes, uint64_t* 
  *          the new residency (host-to-device copies of the planes and LUTs
  *          that become resident; a block that cannot grow in place is moved,
  *          its resident planes copied device to device) and record what the
- *          commit retires.  The layer keeps running at the old bitwidths
+ *          commit retires.  Each range is one hipMemcpyAsync (the copy
+ *          engines move it; no compute unit takes part).  The layer keeps running at the old bitwidths
  *          meanwhile.  APMOE_EBITS for a bitwidth outside {3,4,5,6,16};
  *          APMOE_ENOSPACE (nothing staged, nothing enqueued) when the arena
  *          cannot hold the new blocks even after waiting for retired blocks;
@@ -383,8 +393,9 @@ int apmoe_arena_stats(const apmoe_arena* arena, uint64_t* free_bytes, uint64_t* 
  *          return to the arena once the stream has passed the commit.  All
  *          kernels that read these experts must be ordered on stream.
  *  stats   resident plane and LUT bytes, arena free bytes and largest free
- *          range, and the bytes the last stage copied host to device and
- *          device to device (any pointer may be NULL).
+ *          range, the bytes the last stage copied host to device and device
+ *          to device, and the number of ranges it copied (any pointer may be
+ *          NULL).
  *  destroy waits for outstanding copies and commits; the arena stays the
  *          caller's.
  * Host resources and waits (the pager is the library's one stateful object):
@@ -404,7 +415,7 @@ int apmoe_pager_create(int E, int H, int I, const void* const* host_planes, cons
 int apmoe_pager_stage(apmoe_pager* pager, const int8_t* bits_new, void* copy_stream);
 int apmoe_pager_commit(apmoe_pager* pager, void* stream);
 int apmoe_pager_stats(apmoe_pager* pager, uint64_t* resident_bytes, uint64_t* free_bytes,
-                      uint64_t* largest_free, uint64_t* h2d_bytes, uint64_t* d2d_bytes);
+                      uint64_t* largest_free, uint64_t* h2d_bytes, uint64_t* d2d_bytes, uint64_t* copy_ranges);
 int apmoe_pager_destroy(apmoe_pager* pager);
 
 /*

@@ -39,16 +39,16 @@ def test_validation_before_launch():
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
     # route: k > E, bad scale, null pointers
     big = 1 << 20
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 9, fake, fake, fake, big, None) == _lib.EINVAL
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 0.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL
-    assert lib.apmoe_route(None, 4, 64, fake, None, 1.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL
-    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 300, 2, fake, fake, fake, big, None) == _lib.EINVAL
-    assert lib.apmoe_route(fake, 4, 48, fake, None, 1.0, 8, 2, fake, fake, fake, big, None) == _lib.EINVAL   # H % 32
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 8, 9, fake, fake, None, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 0.0, 8, 2, fake, fake, None, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(None, 4, 64, fake, None, 1.0, 8, 2, fake, fake, None, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 300, 2, fake, fake, None, fake, big, None) == _lib.EINVAL
+    assert lib.apmoe_route(fake, 4, 48, fake, None, 1.0, 8, 2, fake, fake, None, fake, big, None) == _lib.EINVAL   # H % 32
     # a problem too large for the one-kernel router stages logits in the workspace
-    assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, fake,
+    assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, None, fake,
                            4096 * 256 * 8 - 1, None) == _lib.ENOSPACE
-    assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, None, big, None) == _lib.ENOSPACE
-    assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None, 0, None) == _lib.OK   # T = 0
+    assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, None, None, big, None) == _lib.ENOSPACE
+    assert lib.apmoe_route(None, 0, 64, None, None, 1.0, 8, 2, None, None, None, None, 0, None) == _lib.OK   # T = 0
     assert _lib.workspace_bytes(4096, 2, 256, 4096, 64) >= 4096 * 256 * 8   # staged router logits
     # route statistics
     assert lib.apmoe_route_stats(fake, 4, 64, fake, fake, 9, 8, fake, fake, fake, big, None) == _lib.EINVAL   # k > E
@@ -69,11 +69,17 @@ def test_validation_before_launch():
                                      sb.ctypes.data, 2000, 0, 0, now.ctypes.data, out.ctypes.data,
                                      ctypes.byref(stage)) == _lib.EINVAL
     # permute
-    assert lib.apmoe_permute(fake, 4, 0, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
-    assert lib.apmoe_permute(None, 4, 2, 8, 0, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
-    assert lib.apmoe_permute(fake, 4, 2, 8, -1, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL
-    assert lib.apmoe_permute(fake, 4, 2, 250, 7, fake, fake, fake, fake, None, 0, None) == _lib.EINVAL   # E + n > 256
-    assert lib.apmoe_permute(None, 0, 2, 8, 0, None, None, None, None, None, 0, None) == _lib.OK
+    assert lib.apmoe_permute(fake, 4, 0, 8, 0, fake, fake, fake, fake, None, None, None, None, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(None, 4, 2, 8, 0, fake, fake, fake, fake, None, None, None, None, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(fake, 4, 2, 8, -1, fake, fake, fake, fake, None, None, None, None, None, 0, None) == _lib.EINVAL
+    assert lib.apmoe_permute(fake, 4, 2, 250, 7, fake, fake, fake, fake, None, None, None, None, None, 0, None) == _lib.EINVAL   # E + n > 256
+    assert lib.apmoe_permute(None, 0, 2, 8, 0, None, None, None, None, None, None, None, None, None, 0, None) == _lib.OK
+    # permute with routing statistics: wnorm, topk_w and x_norms are required,
+    # and the workspace must hold S * 8 bytes (S = T * (k + n_shared) = 4 * 3)
+    pm = lib.apmoe_permute
+    assert pm(fake, 4, 2, 8, 1, fake, fake, fake, fake, fake, fake, fake, None, fake, big, None) == _lib.EINVAL
+    assert pm(fake, 4, 2, 8, 1, fake, fake, fake, fake, None, fake, fake, fake, fake, big, None) == _lib.EINVAL
+    assert pm(fake, 4, 2, 8, 1, fake, fake, fake, fake, fake, fake, fake, fake, fake, 4 * 3 * 8 - 1, None) == _lib.ENOSPACE
     # gemm: bad stage, H or I not a multiple of 32, mfma_min_tokens < 1
     g = lib.apmoe_bitplane_lut_gemm
     assert g(7, fake, fake, 8, fake, fake, 2, fake, fake, 4, 64, 64, 16, None, 0, None) == _lib.EINVAL

@@ -159,10 +159,13 @@ def test_full_size_layer(name):
           f"groups {sorted(got['counts'].tolist(), reverse=True)[:8]}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen_decode", "mixtral_decode_t8", "e128_decode"])
+@pytest.mark.parametrize("name", ["tiny", "qwen_decode", "mixtral_decode_t8", "e128_decode", "mixtral_prefill"])
 def test_route_stats(name):
-    """Per-expert routing mass and routing-weighted input norm (apmoe_route_stats)
-    against the oracle's statistics over its own routing."""
+    """Per-expert routing mass and routing-weighted input norm against the
+    oracle's statistics over its own routing: as the forward computes them
+    (token norms in the router, sums in the grouping launch; the one-kernel
+    router at Mixtral T = 8, the two-kernel one elsewhere) and as
+    apmoe_route_stats computes them alone."""
     import torch
     cfg = synth.get(name)
     G.say(f"route stats {name}")
@@ -173,13 +176,18 @@ def test_route_stats(name):
     layer, got = G.run_layer(inp, bits)
     if G.check_route(inp, got, ids, gates, logits):
         pytest.skip("a near-tie routed a token differently; its expert's sums legitimately differ")
+    # token norms from the router (fp32 sums of H squares)
+    norms_ref = np.sqrt((inp.x.astype(np.float64) ** 2).sum(axis=1))
+    np.testing.assert_allclose(layer.x_norms[:cfg.T].cpu().numpy(), norms_ref, rtol=1e-5)
+    # the sums the forward's grouping launch computed, then the standalone call
+    fused = [t.cpu().numpy().copy() for t in layer.route_stats()]
     x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
-    mass, wnorm = layer.route_stats(x)
-    torch.cuda.synchronize()
-    # fp32 sums of at most T*k terms
-    np.testing.assert_allclose(mass.cpu().numpy(), mass_ref, rtol=1e-5, atol=1e-5)
-    np.testing.assert_allclose(wnorm.cpu().numpy(), wnorm_ref, rtol=1e-5, atol=1e-4)
-    assert abs(float(mass.sum()) - cfg.T) <= 1e-4 * cfg.T
+    alone = [t.cpu().numpy().copy() for t in layer.route_stats(x)]
+    for mass, wnorm in (fused, alone):
+        # fp32 sums of at most T*k terms
+        np.testing.assert_allclose(mass, mass_ref, rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(wnorm, wnorm_ref, rtol=1e-5, atol=1e-4)
+        assert abs(float(mass.sum()) - cfg.T) <= 1e-4 * cfg.T
 
 
 def test_online_planner_commits_take_effect():

@@ -164,7 +164,7 @@ def test_pager_create_argument_errors():
     assert out.value is None
     for fn in ("apmoe_pager_stage", "apmoe_pager_commit", "apmoe_pager_stats"):
         args = {"apmoe_pager_stage": (None, None, None), "apmoe_pager_commit": (None, None),
-                "apmoe_pager_stats": (None, None, None, None, None, None)}[fn]
+                "apmoe_pager_stats": (None, None, None, None, None, None, None)}[fn]
         assert getattr(lib, fn)(*args) == _lib.EINVAL
     assert lib.apmoe_pager_destroy(None) == _lib.OK
 
