@@ -33,6 +33,18 @@ DESC_WORDS = 18          # 3 matrices x (planes, lut[4], w16) pointers
 DEFAULT_MFMA_MIN_TOKENS = 160
 
 
+def auto_mfma_min_tokens(T: int, k: int, E: int) -> int:
+    """The layer's default path choice: groups of at least
+    DEFAULT_MFMA_MIN_TOKENS slots take the tile path, unless the mean group
+    T * k / E is under half of that, where even a group twice the mean stays
+    on the GEMV side of the crossover: then every group takes the GEMV path
+    and no tile kernel is launched at all (a tile launch that finds no group
+    still costs a few microseconds)."""
+    if T * k < E * (DEFAULT_MFMA_MIN_TOKENS // 2):
+        return 1 << 30
+    return DEFAULT_MFMA_MIN_TOKENS
+
+
 class ExpertTable:
     """Expert weights in device memory plus their descriptor array.
 
@@ -137,12 +149,13 @@ class MoELayer:
     """One MoE expert-FFN layer call on the GPU through libapmoe."""
 
     def __init__(self, E, H, I, k, T, w_router, bias, logit_scale, experts: ExpertTable, bits,
-                 shared: Optional[ExpertTable] = None, shared_I: int = 0, mfma_min_tokens: int = DEFAULT_MFMA_MIN_TOKENS,
+                 shared: Optional[ExpertTable] = None, shared_I: int = 0, mfma_min_tokens: Optional[int] = None,
                  device="cuda"):
         import torch
         self.E, self.H, self.I, self.k, self.T = E, H, I, k, T
         self.logit_scale = float(logit_scale)
-        self.mfma_min_tokens = int(mfma_min_tokens)
+        # None: the default policy (auto_mfma_min_tokens); an explicit value is used as given
+        self.mfma_min_tokens = int(auto_mfma_min_tokens(T, k, E) if mfma_min_tokens is None else mfma_min_tokens)
         self.device = device
         dev = dict(device=device)
         self.w_router = torch.as_tensor(np.ascontiguousarray(w_router), dtype=torch.float32).to(device)
@@ -176,8 +189,9 @@ class MoELayer:
         self.A = torch.empty((S, I), dtype=torch.float16, **dev)
         self.Y = torch.empty((S, H), dtype=torch.float32, **dev)
         self.out = torch.empty((T, H), dtype=torch.float16, **dev)
+        # zeroed: the router keeps its arrival counters at the end (zero between calls)
         nws = _lib.workspace_bytes(T, kk, E2, H, I)
-        self.ws = torch.empty(nws, dtype=torch.uint8, **dev) if nws else None
+        self.ws = torch.zeros(nws, dtype=torch.uint8, **dev) if nws else None
         # routing statistics for the planner (per routed expert), computed in
         # every forward by the router (token norms) and the grouping (sums)
         self.mass = torch.zeros(E, dtype=torch.float32, **dev)
@@ -337,7 +351,7 @@ class OnlinePlanner:
         return status, bits, stage, changed
 
 
-def from_inputs(inp, bits=None, mfma_min_tokens=DEFAULT_MFMA_MIN_TOKENS, device="cuda"):
+def from_inputs(inp, bits=None, mfma_min_tokens=None, device="cuda"):
     """Build device weights and a layer from a generated input set (duck-typed)."""
     cfg = inp.cfg
     experts = ExpertTable(inp.experts, device)

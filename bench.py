@@ -306,8 +306,8 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
     from any_precision_quantized_amd import _lib
     from any_precision_quantized_amd import layer as L
 
-    mfma_min = args.mfma_min_tokens or L.DEFAULT_MFMA_MIN_TOKENS
-    layer = L.from_inputs(inp, bits=bits, mfma_min_tokens=mfma_min)
+    layer = L.from_inputs(inp, bits=bits, mfma_min_tokens=args.mfma_min_tokens)
+    mfma_min = layer.mfma_min_tokens
     x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
     layer.forward(x)
     torch.cuda.synchronize()
@@ -618,7 +618,7 @@ def main():
     inp = synth.make_inputs(cfg, seed=0)
     bits = planned_bits(inp)
     result = measure(args, cfg, inp, bits, args.steps, args.warmup, max(5, min(50, args.steps)))
-    mfma_min = args.mfma_min_tokens or L.DEFAULT_MFMA_MIN_TOKENS
+    mfma_min = args.mfma_min_tokens or L.auto_mfma_min_tokens(cfg.T, cfg.k, cfg.E)
     if not args.no_workloads:
         result["workloads"] = other_workloads(args, cfg.name)
     if not args.no_paging_probe:

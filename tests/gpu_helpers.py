@@ -40,11 +40,11 @@ def inputs(name_or_cfg, seed=0):
     return inp
 
 
-def run_layer(inp, bits, mfma_min_tokens=L.DEFAULT_MFMA_MIN_TOKENS, table=None, shared=None, layer=None):
+def run_layer(inp, bits, mfma_min_tokens=None, table=None, shared=None, layer=None):
     import torch
     if layer is None:
         layer = L.from_inputs(inp, bits=bits, mfma_min_tokens=mfma_min_tokens)
-    else:
+    elif mfma_min_tokens is not None:
         layer.mfma_min_tokens = mfma_min_tokens
     x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
     out = layer.forward(x, table, shared)
