@@ -71,6 +71,7 @@ extern "C" int apmoe_combine(const float* Y, const int32_t* pos_of_slot, const f
     if (T == 0) return APMOE_OK;
     if (!Y || !pos_of_slot || !topk_w || !out) return APMOE_EINVAL;
     dim3 grid((H / 4 + 255) / 256, T);
+    clear_stale_error();
     hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, as_stream(stream), Y, pos_of_slot, topk_w,
                        T, k, n_shared, H, y_shared, reinterpret_cast<half_t*>(out));
     return launch_status();
@@ -83,6 +84,7 @@ extern "C" int apmoe_commit_bits(const int8_t* bits_host, int E, int8_t* bits_de
         if (!valid_bits(bits_host[e])) return APMOE_EBITS;
         a.v[e] = bits_host[e];
     }
+    clear_stale_error();
     hipLaunchKernelGGL(commit_bits_kernel, dim3(1), dim3(APMOE_MAX_EXPERTS), 0, as_stream(stream), a,
                        E, bits_dev);
     return launch_status();
@@ -109,6 +111,7 @@ extern "C" int apmoe_pack_planes(const uint32_t* src, int rows, int cols, uint32
     const char* d0 = reinterpret_cast<const char*>(dst);
     const size_t sb = (size_t)6 * rows * (cols / 32) * 4, db = n * 4;
     if (s0 < d0 + db && d0 < s0 + sb) return APMOE_EINVAL;   // overlapping buffers
+    clear_stale_error();
     hipLaunchKernelGGL(pack_planes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), src,
                        rows, cols, dst);
     return launch_status();

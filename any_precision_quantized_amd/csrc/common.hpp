@@ -120,6 +120,11 @@ __device__ inline float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// hipGetLastError reports the last error of any earlier HIP call on this
+// host thread, not only ours: entry points clear it before their launches so
+// that their status reflects those launches alone.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 inline int launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? APMOE_OK : APMOE_EHIP;
@@ -148,6 +153,16 @@ struct MatView {
     gh16_t* lut;      // [rows][1 << b]
     gh16_t* w16;      // [rows][K]
 };
+
+// A pointer every lane holds the same value of, in scalar registers: buffer
+// resources built from it then need no per-lane loop.
+template <class P>
+__device__ __forceinline__ P uniform_ptr(P p) {
+    const uint64_t u = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return (P)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ inline MatView mat_view(const apmoe_mat& m, int b) {
     MatView v;

@@ -87,6 +87,7 @@ extern "C" int apmoe_exp_decode(const uint32_t* words, uint64_t nwords, const ui
     const uint64_t groups = (n + kGroup - 1) / kGroup;
     const uint64_t wgs = (groups + kDWaves - 1) / kDWaves;
     if (wgs > 0x7FFFFFFFull) return APMOE_EINVAL;
+    clear_stale_error();
     hipLaunchKernelGGL(exp_decode_kernel, dim3((unsigned)wgs), dim3(kDWaves * kWave), 0, as_stream(stream), words,
                        (uint32_t)nwords, block_off, lo, table, n, out);
     return launch_status();

@@ -105,7 +105,11 @@ __device__ __forceinline__ void tile_item(const GemmArgs& a, char* lds, const Ti
     const int hsel = NMAT == 2 ? (wave >> 1) & 1 : 0;   // gate/up: matrix (waves 2, 3: up); down: 0
     const int rowc = min(r0 + tr % kMatRows, rows - 1);
     const apmoe_mat& mt = NMAT == 2 ? (hsel ? a.experts[it.e].up : a.experts[it.e].gate) : a.experts[it.e].down;
-    const MatView mv = mat_view(mt, it.b);
+    MatView mv = mat_view(mt, it.b);
+    // the same matrix for the whole wave: scalar registers, so the buffer
+    // resources need no per-lane loop
+    mv.planes = uniform_ptr(mv.planes);
+    mv.w16 = uniform_ptr(mv.w16);
     // the resource covers the b resident planes only (none at 16 bits)
     const uint32_t pbytes = (uint32_t)(it.b <= kPlanes ? it.b : 0) * (uint32_t)rows * 16u * (uint32_t)nsteps128;
     const uint32_t slab = (uint32_t)rows * 16u * (uint32_t)nsteps128;
@@ -348,6 +352,7 @@ int launch_tile(const GemmArgs& a, hipStream_t s) {
     const long long groups = std::min<long long>(a.E, S / a.mfma_min_tokens);
     const long long items = ((S + kTToks - 1) / kTToks + groups) * RT;
     if (items <= 0) return APMOE_OK;
+    clear_stale_error();
     if (gu)
         hipLaunchKernelGGL(tile_kernel<2>, dim3((unsigned)items), dim3(kThreadsTile), 0, s, a, RT);
     else

@@ -753,6 +753,7 @@ int launch_gemv(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return APMOE_EHIP;
+    clear_stale_error();
     if (gu)
         hipLaunchKernelGGL(gemv_kernel<2>, grid, block, 0, s, a, KS, partial, ncu);
     else

@@ -257,6 +257,7 @@ extern "C" int apmoe_pager_commit(apmoe_pager* pg, void* stream) {
                      (size_t)reinterpret_cast<PatchHeader*>(pg->host_buf)->n_patch * sizeof(Patch) + pg->E;
     char* dbuf = pg->base + pg->dev_buf;
     if (hipMemcpyAsync(dbuf, pg->host_buf, n, hipMemcpyHostToDevice, s) != hipSuccess) return APMOE_EHIP;
+    clear_stale_error();
     hipLaunchKernelGGL(pager_commit_kernel, dim3(16), dim3(256), 0, s, dbuf, pg->bits_dev);
     int rc = launch_status();
     if (rc != APMOE_OK) return rc;

@@ -1,93 +1,42 @@
 // Router: top-k over the router logits, then a softmax over the k chosen.
 //
-// A few tokens over a small router matrix run one kernel (route_kernel): a
-// workgroup takes one token, computes its logits for every expert
-// into LDS and selects from there, so no logit leaves the CU and the layer
-// pays one launch.  Everything else runs two kernels.  The logits kernel tiles
-// (TB tokens x 8 experts) per workgroup: wave w owns experts 2w, 2w+1 of the
-// tile and its lanes split the hidden dimension (four columns each per 256),
-// so one 16-byte router-weight load feeds TB tokens and the tile's weights and
-// activations cross the CU once.  TB is 4 unless that leaves fewer than two
-// workgroups per CU; then 2, or 1 (router load latency is hidden by more
-// workgroups, not by longer tiles: at 64 tokens x 60 experts, 512 one-token
-// tiles route in 12.2 us against 15.1 us for 128 four-token tiles; at 256
-// tokens x 128 experts four-token tiles are the fastest).
-// Products and sums are fp64 (an fp16 x fp32 product is exact in fp64); each
-// lane's partial sums meet in a fixed reduction order, so a logit never depends
-// on scheduling.  The logits go to the workspace; the select kernel then runs
-// one wave per token: k rounds of a wave-wide argmax (ties to the lower
-// expert), then the softmax over the k chosen logits in fp64.
+// Logits are sums of fp16 x fp32 products, each exact in fp64, summed in
+// fp64.  Three launch shapes:
+//  * A few tokens over a small router matrix (route_fused_kernel): a
+//    workgroup takes one token, its 16 waves sum the logits of every expert
+//    on the vector fp64 units into LDS and it selects from there, so no logit
+//    leaves the CU and the layer pays one launch.  The matrix cores would pad
+//    one token to sixteen.
+//  * Otherwise the logits run on the fp64 matrix cores (logits_kernel):
+//    v_mfma_f64_16x16x4 takes a 16-token x 16-expert tile four hidden columns
+//    at a time.  A workgroup of 16 waves owns one (token tile, expert tile,
+//    K chunk); the hidden dimension is cut into 32-column units dealt evenly
+//    to the KC * 16 waves of a tile, and lane (r, g) = (lane % 16, lane / 16)
+//    loads 8 columns of token row r (one 16-byte load) and of expert row r
+//    (two) per unit, the lane groups g = 0..3 being the four K rows of the
+//    eight matrix steps.  The 16 wave tiles meet in LDS in wave order.
+//  * When one expert tile and one chunk cover a token tile, that workgroup
+//    selects at once (wave w: token w); otherwise it stores its partial tile
+//    and select_kernel (one wave per token) adds the KC partials in chunk
+//    order, so a logit never depends on scheduling, and selects.  A second
+//    launch is cheaper here than a last-arriving-workgroup finish: the
+//    agent-scope fences that would make the partials visible across XCDs
+//    cost more than the launch.
+// Selection: k rounds of a wave-wide argmax (ties to the lower expert), then
+// the softmax over the k chosen logits in fp64.  Token norms (fp32 squares in
+// a fixed order) come from the x values already loaded: the waves of expert
+// tile 0, or of expert group 0 in the one-token kernel.
 #include "common.hpp"
 
 namespace apmoe {
 namespace {
 
-constexpr int kEPW = 2;                 // experts per wave
-constexpr int kRWaves = 4;
-constexpr int kEB = kEPW * kRWaves;     // experts per logits tile
+constexpr int kRt = 16;        // tokens and experts per tile
+constexpr int kRtWaves = 16;   // waves per workgroup
+constexpr int kUnit = 32;      // hidden columns per unit (four lane groups x 8)
 
+typedef double double4v_t __attribute__((ext_vector_type(4)));
 typedef float float4v_t __attribute__((ext_vector_type(4)));
-
-template <int kTB>
-__global__ __launch_bounds__(kRWaves * kWave) void logits_kernel(const half_t* __restrict__ x, int T, int H,
-                                                                  const float* __restrict__ w_router,
-                                                                  const float* __restrict__ bias, float scale,
-                                                                  int E, double* __restrict__ L,
-                                                                  float* __restrict__ norms) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lane = threadIdx.x % kWave;
-    const int t0 = blockIdx.x * kTB;
-    const int e0 = blockIdx.y * kEB + wave * kEPW;
-    // rows past T or E read a valid row; their sums are never written
-    const half_t* xr[kTB];
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) xr[j] = x + (size_t)min(t0 + j, T - 1) * H;
-    const float* wr[kEPW];
-#pragma unroll
-    for (int j = 0; j < kEPW; ++j) wr[j] = w_router + (size_t)min(e0 + j, E - 1) * H;
-
-    double acc[kTB][kEPW];
-    float sq[kTB];   // ||x_t||^2 on the first expert tile's first wave (the same order as norms_kernel)
-    const bool do_norm = norms && blockIdx.y == 0 && wave == 0;
-#pragma unroll
-    for (int t = 0; t < kTB; ++t) {
-        sq[t] = 0.f;
-#pragma unroll
-        for (int j = 0; j < kEPW; ++j) acc[t][j] = 0.0;
-    }
-#pragma unroll 2
-    for (int h = 4 * lane; h < H; h += 4 * kWave) {   // H % 32 == 0: h + 3 < H
-        float4v_t wv[kEPW];
-#pragma unroll
-        for (int j = 0; j < kEPW; ++j) wv[j] = *reinterpret_cast<const float4v_t*>(wr[j] + h);
-#pragma unroll
-        for (int t = 0; t < kTB; ++t) {
-            const half4_t xv = *reinterpret_cast<const half4_t*>(xr[t] + h);
-#pragma unroll
-            for (int j = 0; j < kEPW; ++j)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[t][j] = fma((double)xv[c], (double)wv[j][c], acc[t][j]);
-            if (do_norm)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) sq[t] = fmaf((float)xv[c], (float)xv[c], sq[t]);
-        }
-    }
-    if (do_norm)
-#pragma unroll
-        for (int t = 0; t < kTB; ++t) {
-            const float n2 = wave_sum(sq[t]);
-            if (lane == 0 && t0 + t < T) norms[t0 + t] = sqrtf(n2);
-        }
-#pragma unroll
-    for (int t = 0; t < kTB; ++t)
-#pragma unroll
-        for (int j = 0; j < kEPW; ++j) {
-            const double s = wave_sum(acc[t][j]);
-            const int tt = t0 + t, e = e0 + j;
-            if (lane == 0 && tt < T && e < E)
-                L[(size_t)tt * E + e] = (double)scale * (s + (bias ? (double)bias[e] : 0.0));
-        }
-}
 
 // k rounds of a wave-wide argmax over v (lane's experts lane + 64c), ties to
 // the lower expert, then the softmax over the chosen logits in fp64: lane j
@@ -125,6 +74,102 @@ __device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int
     for (int j = lane; j < k; j += kWave) topk_w[(size_t)t * k + j] = (float)(exp(chosen[j] - lmax) / sum);
 }
 
+// Grid: blockIdx.x = (tt * ET + et) * KC + kc.  part: [TT][KC][16][16 ET]
+// fp64 partial logits and npart: [TT][KC][16] fp32 partial squares (both only
+// when ET * KC > 1, for select_kernel).
+__global__ __launch_bounds__(kRtWaves * kWave) void logits_kernel(
+    const half_t* __restrict__ x, int T, int H, const float* __restrict__ w_router, const float* __restrict__ bias,
+    float scale, int E, int k, int ET, int KC, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    float* __restrict__ norms, double* __restrict__ part, float* __restrict__ npart) {
+    __shared__ double red[kRtWaves * kRt * kRt];   // the waves' tiles, then the token tile's logits [16][16]
+    __shared__ float nred[kRtWaves][4][kRt];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int r = lane % kRt, g = lane / kRt;
+    const int kc = blockIdx.x % KC;
+    const int et = (blockIdx.x / KC) % ET;
+    const int tt = blockIdx.x / KC / ET;
+    const int t0 = tt * kRt, e0 = et * kRt;
+    const int U = H / kUnit;
+    const int slices = KC * kRtWaves, slice = kc * kRtWaves + wave;
+    const int u0 = (int)((long long)slice * U / slices), u1 = (int)((long long)(slice + 1) * U / slices);
+    const bool nrm = norms && et == 0;   // uniform over the workgroup
+    // rows past T or E read a valid row; their sums are never used
+    const half_t* xr = x + (size_t)min(t0 + r, T - 1) * H + 8 * g;
+    const float* wr = w_router + (size_t)min(e0 + r, E - 1) * H + 8 * g;
+    // one unit's loads in flight while the previous unit is multiplied (46
+    // VGPRs: two 16-wave workgroups fit a CU); two accumulators halve the
+    // dependent MFMA chain and meet in a fixed order
+    half8_t xn = {};
+    float4_t wan = {}, wbn = {};
+    if (u0 < u1) {
+        xn = *reinterpret_cast<const half8_t*>(xr + (size_t)kUnit * u0);
+        wan = *reinterpret_cast<const float4_t*>(wr + (size_t)kUnit * u0);
+        wbn = *reinterpret_cast<const float4_t*>(wr + (size_t)kUnit * u0 + 4);
+    }
+    double4v_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
+    float sq = 0.f;
+    for (int u = u0; u < u1; ++u) {
+        const half8_t xv = xn;
+        const float4_t wa = wan, wb = wbn;
+        if (u + 1 < u1) {
+            xn = *reinterpret_cast<const half8_t*>(xr + (size_t)kUnit * (u + 1));
+            wan = *reinterpret_cast<const float4_t*>(wr + (size_t)kUnit * (u + 1));
+            wbn = *reinterpret_cast<const float4_t*>(wr + (size_t)kUnit * (u + 1) + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[i], (double)(i < 4 ? wa[i] : wb[i - 4]), acc0,
+                                                        0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[i + 1], (double)(i < 4 ? wa[i + 1] : wb[i - 3]),
+                                                        acc1, 0, 0, 0);
+        }
+        if (nrm)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sq = fmaf((float)xv[i], (float)xv[i], sq);
+    }
+    const double4v_t acc = acc0 + acc1;
+    // the fp64 16x16 result: lane (r, g) holds tokens g, g + 4, g + 8, g + 12 of
+    // the tile for expert r (register v is token 4v + g)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave * kRt * kRt + (4 * v + g) * kRt + r] = acc[v];
+    if (nrm) nred[wave][g][r] = sq;
+    __syncthreads();
+    const int i = threadIdx.x;   // element (token i / 16, expert i % 16) of the tile
+    double tile = 0.0;
+    float nq = 0.f;
+    if (i < kRt * kRt)
+#pragma unroll
+        for (int w = 0; w < kRtWaves; ++w) tile += red[w * kRt * kRt + i];
+    if (nrm && i < kRt)
+#pragma unroll
+        for (int w = 0; w < kRtWaves; ++w) nq += (nred[w][0][i] + nred[w][1][i]) + (nred[w][2][i] + nred[w][3][i]);
+    if (ET * KC > 1) {   // uniform: select_kernel finishes
+        double* pt = part + (size_t)(tt * KC + kc) * kRt * (ET * kRt);
+        if (i < kRt * kRt) pt[(i / kRt) * (ET * kRt) + e0 + i % kRt] = tile;
+        if (nrm && i < kRt) npart[(size_t)(tt * KC + kc) * kRt + i] = nq;
+        return;
+    }
+    double* L = red;   // [16][16]
+    __syncthreads();   // every wave has read red
+    if (i < kRt * kRt) L[i] = tile;
+    if (nrm && i < kRt && t0 + i < T) norms[t0 + i] = sqrtf(nq);
+    constexpr int Ep = kRt;
+    __syncthreads();
+    const int t = t0 + wave;
+    if (t >= T) return;   // uniform over the wave; no barrier follows
+    constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
+    double* row = L + wave * Ep;
+    double v[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int e = lane + kWave * c;
+        v[c] = e < E ? (double)scale * (row[e] + (bias ? (double)bias[e] : 0.0)) : -__builtin_inf();
+    }
+    // the row is this wave's alone from here: its first k entries take the chosen logits
+    select_topk<kPer>(v, E, k, t, lane, row, topk_ids, topk_w);
+}
+
 // Fused router: TB tokens per workgroup, all E logits in LDS, then select.
 // Sixteen waves: wave w sums the hidden-dimension quarter w % 4 for the
 // expert group w / 4 (experts in chunks of EC, chunk g, g + 4, ...), its lanes
@@ -133,7 +178,7 @@ __device__ __forceinline__ void select_topk(double (&v)[kPer], int E, int k, int
 // (P[0] becomes the logits), then k chosen logits per wave.
 constexpr int kFWaves = 16;
 template <int TB>
-__global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __restrict__ x, int T, int H,
+__global__ __launch_bounds__(kFWaves * kWave) void route_fused_kernel(const half_t* __restrict__ x, int T, int H,
                                                                  const float* __restrict__ w_router,
                                                                  const float* __restrict__ bias, float scale, int E,
                                                                  int k, int32_t* __restrict__ topk_ids,
@@ -222,22 +267,52 @@ __global__ __launch_bounds__(kFWaves * kWave) void route_kernel(const half_t* __
     }
 }
 
+// One wave per token of the logits kernel's partial tiles: the KC partials
+// of each logit added in chunk order, then the selection.
 constexpr int kSelWaves = 1;   // one-wave workgroups spread the tokens over the most CUs
 
-__global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double* __restrict__ L, int T, int E, int k,
+__global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double* __restrict__ part,
+                                                                    const float* __restrict__ npart, int T, int E,
+                                                                    int k, int ET, int KC,
+                                                                    const float* __restrict__ bias, float scale,
                                                                     int32_t* __restrict__ topk_ids,
-                                                                    float* __restrict__ topk_w) {
+                                                                    float* __restrict__ topk_w,
+                                                                    float* __restrict__ norms) {
     __shared__ double chosen[kSelWaves][APMOE_MAX_EXPERTS];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * kSelWaves + wave;
     if (t >= T) return;   // uniform over the wave; no block barrier follows
+    const int tt = t / kRt, tr = t % kRt, Ep = ET * kRt;
+    const double* p0 = part + ((size_t)tt * KC * kRt + tr) * Ep;
     constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
+    // each logit adds its KC partials in chunk order; the loads of every
+    // expert column go out together
     double v[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) v[c] = 0.0;
+#pragma unroll 4
+    for (int q = 0; q < KC; ++q)
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) {
+            const int e = lane + kWave * c;
+            if (e < E) v[c] += p0[(size_t)q * kRt * Ep + e];
+        }
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         const int e = lane + kWave * c;
-        v[c] = e < E ? L[(size_t)t * E + e] : -__builtin_inf();
+        v[c] = e < E ? (double)scale * (v[c] + (bias ? (double)bias[e] : 0.0)) : -__builtin_inf();
+    }
+    if (norms) {   // lane q loads chunk q's partial; the wave adds them in chunk order
+        float sm = 0.f;
+        for (int q0 = 0; q0 < KC; q0 += kWave) {
+            const int q = q0 + lane;
+            const float pv = q < KC ? npart[((size_t)tt * KC + q) * kRt + tr] : 0.f;
+            const int n = min(kWave, KC - q0);
+            for (int j = 0; j < n; ++j)
+                sm += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), j));
+        }
+        if (lane == 0) norms[t] = sqrtf(sm);
     }
     select_topk<kPer>(v, E, k, t, lane, chosen[wave], topk_ids, topk_w);
 }
@@ -330,9 +405,39 @@ int fused_tokens(int T, int E, int H) {
     return (wbytes <= 160.0 * 1024 && lds <= 65536.0) ? tb : 0;
 }
 
+// Matrix-core shape: TT token tiles x ET expert tiles x KC chunks of the
+// hidden dimension.  The fp64 MFMA work of a small router still needs many
+// CUs (64 tokens x 60 experts x 2048 on 16 CUs take 3.4 us of MFMA time), so
+// KC aims at about 256 workgroups, as far as every wave keeps a unit.
+struct RoutePlan {
+    int TT, ET, KC;
+    size_t part_bytes;   // partial logits + partial squares (0: one launch)
+};
+
+RoutePlan route_plan(int T, int E, int H) {
+    RoutePlan p{};
+    p.TT = (T + kRt - 1) / kRt;
+    p.ET = (E + kRt - 1) / kRt;
+    const long long J = (long long)p.TT * p.ET;
+    const int U = H / kUnit;
+    p.KC = (int)std::min<long long>((256 + J - 1) / J, std::max(1, U / kRtWaves));
+    if ((long long)p.ET * p.KC > 1) {
+        const size_t logits = (size_t)p.TT * p.KC * kRt * p.ET * kRt * sizeof(double);
+        const size_t sq = (size_t)p.TT * p.KC * kRt * sizeof(float);
+        p.part_bytes = (logits + sq + 255) / 256 * 256;
+    }
+    return p;
+}
+
+// The most any router of up to E experts needs (the need is not monotone in
+// E, and one workspace may serve a router over fewer experts than it was
+// sized for).
 size_t route_workspace_bytes(int T, int E, int H) {
-    if (T <= 0 || E <= 0 || H <= 0 || fused_tokens(T, E, H)) return 0;
-    return (size_t)T * (size_t)E * sizeof(double);
+    if (T <= 0 || E <= 0 || H <= 0) return 0;
+    size_t m = 0;
+    for (int e = 1; e <= E; ++e)
+        if (!fused_tokens(T, e, H)) m = std::max(m, route_plan(T, e, H).part_bytes);
+    return m;
 }
 
 }  // namespace apmoe
@@ -346,41 +451,33 @@ extern "C" int apmoe_route(const uint16_t* x, int T, int H, const float* w_route
     if (!(logit_scale > 0.0f)) return APMOE_EINVAL;
     if (T == 0) return APMOE_OK;
     if (!x || !w_router || !topk_ids || !topk_w) return APMOE_EINVAL;
+    if ((uintptr_t)x % 16 || (uintptr_t)w_router % 16) return APMOE_EINVAL;
+    if ((long long)T * k > (1ll << 30)) return APMOE_EINVAL;
     hipStream_t s = as_stream(stream);
     const half_t* xh = reinterpret_cast<const half_t*>(x);
-    switch (fused_tokens(T, E, H)) {
-#define APMOE_ROUTE_FUSED(TB_)                                                                                \
-    case TB_:                                                                                                 \
-        hipLaunchKernelGGL(route_kernel<TB_>, dim3((T + TB_ - 1) / TB_), dim3(kFWaves * kWave),                \
-                           (4 * TB_ * E + kFWaves * k) * sizeof(double), s, xh, T, H, w_router, bias, logit_scale, \
-                           E, k, topk_ids, topk_w, x_norms);                                                  \
+    if (fused_tokens(T, E, H)) {
+        clear_stale_error();
+        hipLaunchKernelGGL(route_fused_kernel<1>, dim3(T), dim3(kFWaves * kWave), (4 * E + kFWaves * k) * sizeof(double),
+                           s, xh, T, H, w_router, bias, logit_scale, E, k, topk_ids, topk_w, x_norms);
         return launch_status();
-        APMOE_ROUTE_FUSED(1)
-#undef APMOE_ROUTE_FUSED
-        default: break;
     }
-    if (!ws || ws_bytes < route_workspace_bytes(T, E, H)) return APMOE_ENOSPACE;
-    double* L = reinterpret_cast<double*>(ws);
-    const int etiles = (E + kEB - 1) / kEB;
-    int ncu = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return APMOE_EHIP;
-    auto tiles = [&](int tb) { return (long long)((T + tb - 1) / tb) * etiles; };
-    const int tb = tiles(4) >= 2LL * ncu ? 4 : tiles(2) >= 2LL * ncu ? 2 : 1;
-    const dim3 grid((T + tb - 1) / tb, etiles);
-    if (tb == 4)
-        hipLaunchKernelGGL(logits_kernel<4>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
-                           E, L, x_norms);
-    else if (tb == 2)
-        hipLaunchKernelGGL(logits_kernel<2>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
-                           E, L, x_norms);
-    else
-        hipLaunchKernelGGL(logits_kernel<1>, grid, dim3(kRWaves * kWave), 0, s, xh, T, H, w_router, bias, logit_scale,
-                           E, L, x_norms);
+    const RoutePlan p = route_plan(T, E, H);
+    double* part = nullptr;
+    float* npart = nullptr;
+    if (p.part_bytes) {
+        if (!ws || (uintptr_t)ws % 8 || ws_bytes < p.part_bytes) return APMOE_ENOSPACE;
+        part = reinterpret_cast<double*>(ws);
+        npart = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                         (size_t)p.TT * p.KC * kRt * p.ET * kRt * sizeof(double));
+    }
+    const long long blocks = (long long)p.TT * p.ET * p.KC;
+    clear_stale_error();
+    hipLaunchKernelGGL(logits_kernel, dim3((unsigned)blocks), dim3(kRtWaves * kWave), 0, s, xh, T, H, w_router, bias,
+                       logit_scale, E, k, p.ET, p.KC, topk_ids, topk_w, x_norms, part, npart);
     int rc = launch_status();
-    if (rc != APMOE_OK) return rc;
-    hipLaunchKernelGGL(select_kernel, dim3((T + kSelWaves - 1) / kSelWaves), dim3(kSelWaves * kWave), 0, s, L, T, E,
-                       k, topk_ids, topk_w);
+    if (rc != APMOE_OK || !p.part_bytes) return rc;
+    hipLaunchKernelGGL(select_kernel, dim3((T + kSelWaves - 1) / kSelWaves), dim3(kSelWaves * kWave), 0, s, part,
+                       npart, T, E, k, p.ET, p.KC, bias, logit_scale, topk_ids, topk_w, x_norms);
     return launch_status();
 }
 
@@ -395,11 +492,13 @@ extern "C" int apmoe_route_stats(const uint16_t* x, int T, int H, const int32_t*
     hipStream_t s = as_stream(stream);
     float* norms = reinterpret_cast<float*>(ws);
     if (T > 0) {
+        clear_stale_error();
         hipLaunchKernelGGL(norms_kernel, dim3((T + 3) / 4), dim3(4 * kWave), 0, s, reinterpret_cast<const half_t*>(x),
                            T, H, norms);
         const int rc = launch_status();
         if (rc != APMOE_OK) return rc;
     }
+    clear_stale_error();
     hipLaunchKernelGGL(stats_kernel, dim3(E), dim3(kStatThreads), 0, s, topk_ids, topk_w, T * k, k, norms, mass,
                        wnorm);
     return launch_status();

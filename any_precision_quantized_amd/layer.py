@@ -189,9 +189,8 @@ class MoELayer:
         self.A = torch.empty((S, I), dtype=torch.float16, **dev)
         self.Y = torch.empty((S, H), dtype=torch.float32, **dev)
         self.out = torch.empty((T, H), dtype=torch.float16, **dev)
-        # zeroed: the router keeps its arrival counters at the end (zero between calls)
         nws = _lib.workspace_bytes(T, kk, E2, H, I)
-        self.ws = torch.zeros(nws, dtype=torch.uint8, **dev) if nws else None
+        self.ws = torch.empty(nws, dtype=torch.uint8, **dev) if nws else None
         # routing statistics for the planner (per routed expert), computed in
         # every forward by the router (token norms) and the grouping (sums)
         self.mass = torch.zeros(E, dtype=torch.float32, **dev)

@@ -105,11 +105,13 @@ typedef struct apmoe_expert {
  *           fixed order), computed from the x rows the router already reads;
  *           apmoe_permute turns them into the planner's routing statistics.
  *  ws/ws_bytes  workspace of at least apmoe_workspace_bytes(T, k, E, H, I)
- *           bytes.  Small problems (a token group's share of T * E * H
- *           multiply-adds fits one workgroup) keep the logits on chip and
- *           need none; larger ones stage the fp64 logits there (T * E * 8
- *           bytes) and return APMOE_ENOSPACE if it is short.
- * Needs 1 <= k <= E <= APMOE_MAX_EXPERTS, H > 0 and H % 32 == 0.
+ *           bytes, 8-byte aligned.  A few tokens over a small router matrix,
+ *           or a single 16-expert tile with an unsplit hidden dimension, need
+ *           none; otherwise partial fp64 logits are staged there for a
+ *           second launch that adds them and selects.  APMOE_ENOSPACE if
+ *           the buffer is short.
+ * x and w_router must be 16-byte aligned.  Needs 1 <= k <= E <=
+ * APMOE_MAX_EXPERTS, H > 0, H % 32 == 0 and T * k <= 2^30.
  */
 int apmoe_route(const uint16_t* x, int T, int H, const float* w_router, const float* bias,
                 float logit_scale, int E, int k, int32_t* topk_ids, float* topk_w, float* x_norms,
@@ -312,8 +314,9 @@ int apmoe_plan_online(int E, int L, const int8_t* levels, const double* harm, co
                       uint64_t m_kv, uint64_t hysteresis, const int8_t* bits_now, int8_t* bits_out,
                       int* stage_out);
 
-/* Workspace bytes apmoe_route and apmoe_bitplane_lut_gemm need for these
- * shapes (one buffer serves both; calls that share it must not overlap). */
+/* Workspace bytes apmoe_route (over up to E experts) and
+ * apmoe_bitplane_lut_gemm need for these shapes (one buffer serves both;
+ * calls that share it must not overlap). */
 size_t apmoe_workspace_bytes(int T, int k, int E, int H, int I);
 
 /* uint32 words of all six packed planes of a rows x cols matrix:

@@ -44,7 +44,9 @@ def test_validation_before_launch():
     assert lib.apmoe_route(None, 4, 64, fake, None, 1.0, 8, 2, fake, fake, None, fake, big, None) == _lib.EINVAL
     assert lib.apmoe_route(fake, 4, 64, fake, None, 1.0, 300, 2, fake, fake, None, fake, big, None) == _lib.EINVAL
     assert lib.apmoe_route(fake, 4, 48, fake, None, 1.0, 8, 2, fake, fake, None, fake, big, None) == _lib.EINVAL   # H % 32
-    # a problem too large for the one-kernel router stages logits in the workspace
+    assert lib.apmoe_route(ctypes.c_void_p(0x1002), 4, 64, fake, None, 1.0, 8, 2, fake, fake, None, fake, big,
+                           None) == _lib.EINVAL   # x not 16-byte aligned
+    # partial logits of several expert tiles are staged in the workspace
     assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, None, fake,
                            4096 * 256 * 8 - 1, None) == _lib.ENOSPACE
     assert lib.apmoe_route(fake, 4096, 4096, fake, None, 1.0, 256, 2, fake, fake, None, None, big, None) == _lib.ENOSPACE
@@ -94,7 +96,8 @@ def test_validation_before_launch():
     assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, 1 << 18, 4096, 64, 16, fake, big, None) == _lib.EINVAL
     assert g(1, fake, fake, 8, fake, fake, 2, fake, fake, 1 << 16, 64, 8192, 16, fake, big, None) == _lib.EINVAL
     assert g(1, fake, fake, 8, fake, fake, 2, fake, fake, 4, 32768, 32768, 16, fake, big, None) == _lib.EINVAL
-    assert g(0, fake, fake, 8, fake, fake, 2, fake, fake, (1 << 18) - 1, 4096, 64, 16, fake, 0, None) == _lib.ENOSPACE
+    # (over 32 experts, whose router stages partial logits, so the workspace is not empty)
+    assert g(0, fake, fake, 32, fake, fake, 2, fake, fake, (1 << 18) - 1, 4096, 64, 16, fake, 0, None) == _lib.ENOSPACE
     # the allocation-free stage refuses shapes whose split-K partials exceed its
     # static scratch before touching the GPU: 16384 tokens over 4 experts of 64
     # rows, K = 14336 split in 4: 4 * 16384 * 2 * 64 * 4 bytes = 32 MiB > 16 MiB
@@ -157,3 +160,16 @@ def test_host_planner_rejects_bad_inputs():
     assert st == _lib.EINVAL
     st, _ = _lib.plan_bitwidths([6, 5, 4], np.zeros((2, 3)), np.array([[3, 2, 1]] * 2), [3, 4], 10)
     assert st == _lib.EINVAL
+
+
+def test_workspace_covers_routers_over_fewer_experts():
+    """One workspace serves the router over the routed experts and the expert
+    stages over routed + always-on experts: the size never shrinks as E grows,
+    and the router's counters sit past the GEMM's bytes."""
+    for T in (1, 16, 64, 256, 8192):
+        for H in (256, 2048, 2816, 4096):
+            prev = 0
+            for E in range(1, 257):
+                n = _lib.workspace_bytes(T, 2, E, H, 1408)
+                assert n >= prev, (T, H, E)
+                prev = n
