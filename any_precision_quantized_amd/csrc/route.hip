@@ -286,18 +286,31 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
     const int tt = t / kRt, tr = t % kRt, Ep = ET * kRt;
     const double* p0 = part + ((size_t)tt * KC * kRt + tr) * Ep;
     constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
-    // each logit adds its KC partials in chunk order; the loads of every
-    // expert column go out together
+    // each logit adds its KC partials in chunk order; the loads carry no
+    // condition (columns past Ep re-read column Ep - 1, never used), so the
+    // compiler issues a whole unrolled group of them before the first add
     double v[kPer];
+    int ec[kPer];
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) v[c] = 0.0;
-#pragma unroll 4
-    for (int q = 0; q < KC; ++q)
+    for (int c = 0; c < kPer; ++c) {
+        v[c] = 0.0;
+        ec[c] = min(lane + kWave * c, Ep - 1);
+    }
+    constexpr int kQB = 4;   // chunks whose loads go out together
+    for (int q0 = 0; q0 < KC; q0 += kQB) {
+        double tq[kQB][kPer];
 #pragma unroll
-        for (int c = 0; c < kPer; ++c) {
-            const int e = lane + kWave * c;
-            if (e < E) v[c] += p0[(size_t)q * kRt * Ep + e];
+        for (int j = 0; j < kQB; ++j) {
+            const double* pq = p0 + (size_t)min(q0 + j, KC - 1) * kRt * Ep;
+#pragma unroll
+            for (int c = 0; c < kPer; ++c) tq[j][c] = pq[ec[c]];
         }
+#pragma unroll
+        for (int j = 0; j < kQB; ++j)
+            if (q0 + j < KC)   // uniform
+#pragma unroll
+                for (int c = 0; c < kPer; ++c) v[c] += tq[j][c];
+    }
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         const int e = lane + kWave * c;
