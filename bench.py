@@ -413,7 +413,7 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
         torch.cuda.synchronize()
         per[name] = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3   # us
     dominant = max(names, key=lambda n: per[n])
-    route_stats_us = None
+    route_stats_us = route_stats_in_step_us = None
     if time_stats:
         # routing statistics for the planner (outside the layer step: the planner
         # reads them at a step boundary), timed the same way
@@ -427,6 +427,34 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
                 raise _lib.ApmoeError(rc, "route_stats")
         torch.cuda.synchronize()
         route_stats_us = sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3
+
+        # what the statistics cost inside the step: router + grouping with the
+        # token norms and per-expert sums, against the same two launches without
+        def pair(stats):
+            nrm = p(layer.x_norms) if stats else None
+            rc = lib.apmoe_route(p(x), T, H, p(layer.w_router), p(layer.bias), layer.logit_scale, E, k,
+                                 p(layer.topk_ids), p(layer.topk_w), nrm, ws, wsb, sp)
+            if rc == 0:
+                rc = lib.apmoe_permute(p(layer.topk_ids), T, k, E, nsh, p(layer.counts), p(layer.offsets),
+                                       p(layer.sorted_slots), p(layer.pos_of_slot),
+                                       p(layer.topk_w) if stats else None, nrm,
+                                       p(layer.mass) if stats else None, p(layer.wnorm) if stats else None,
+                                       p(layer.ws_stats) if stats else None,
+                                       layer.ws_stats.numel() if stats else 0, sp)
+            if rc != 0:
+                raise _lib.ApmoeError(rc, "route + permute")
+
+        pair_us = {}
+        for stats in (False, True, False, True):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(probe_steps)]
+            for i in range(probe_steps):
+                evs[i][0].record(stream)
+                pair(stats)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            pair_us.setdefault(stats, []).append(sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3)
+        route_stats_in_step_us = float(np.mean(pair_us[True]) - np.mean(pair_us[False]))
 
     # Timed region: K whole steps; the dominant launch is bracketed by events.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -498,6 +526,7 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
         "roofline": roofline,
         "per_launch_us": {n: round(per[n], 2) for n in names},
         "route_stats_us": None if route_stats_us is None else round(route_stats_us, 2),
+        "route_stats_in_step_us": None if route_stats_in_step_us is None else round(route_stats_in_step_us, 2),
         "per_launch_bytes": {n: int(by.get(n, 0)) for n in names},
     }
     gu, dn = per.get("gate_up_gemv"), per.get("down_gemv")
