@@ -5,9 +5,19 @@
 // 4096-entry table in LDS, and writes weight g * 16384 + 64 j + l = (symbol
 // << 8) | its raw low byte, so every store of the wave covers 64 consecutive
 // weights (128 bytes) and every low-byte load 64 consecutive bytes.  A lane
-// keeps a 64-bit window of its stream and refills it one 32-bit word at a
-// time from a word it loaded at the previous refill, and works in chunks of
-// 16 steps whose raw low bytes it loads and whose weights it stores together.  The stream is
+// keeps a 64-bit window of its stream and shifts in one 32-bit word whenever
+// 32 bits are used up.  The steps go in chunks of 16 (at most 16 x 12 bits,
+// so at most six words are shifted in per chunk).  The words a chunk shifts
+// in come from LDS: at the start of chunk c the lane loads the 13 words from
+// two past its current word (a superset of what chunk c + 1 can need, since
+// chunk c moves it at most six words on) into registers, and after chunk c's
+// steps, before its stores, it writes them to its slot of a two-slot LDS
+// window for chunk c + 1.  A step's refill is then an LDS read, and the only
+// waits on global loads fall at chunk ends, a whole chunk after the loads
+// went out and never behind a store.  (Loading the
+// next word from global memory at each refill made every refill wait for the
+// previous one's load: the compiler cannot count loads across the
+// data-dependent refill branch, so it waited for all of them.)  The stream is
 // read through a buffer resource of nwords words: words past the end (and
 // anything a malformed stream points at) read as zeros.
 #include "common.hpp"
@@ -20,6 +30,9 @@ constexpr int kDWaves = 4;
 constexpr int kLmax = 12;
 constexpr int kS = 256;
 constexpr int kGroup = kWave * kS;
+constexpr int kC = 16;        // steps per chunk
+constexpr int kWin = 13;      // words staged per chunk
+constexpr int kWinPad = 16;   // LDS words per lane and slot
 
 __global__ __launch_bounds__(kDWaves * kWave) void exp_decode_kernel(const uint32_t* __restrict__ words,
                                                                      uint32_t nwords,
@@ -28,6 +41,7 @@ __global__ __launch_bounds__(kDWaves * kWave) void exp_decode_kernel(const uint3
                                                                      const uint16_t* __restrict__ table, uint64_t n,
                                                                      uint16_t* __restrict__ out) {
     __shared__ uint16_t tab[1 << kLmax];
+    __shared__ uint32_t win[kDWaves][2][kWinPad][kWave];   // [wave][slot][word][lane]: lanes on distinct banks
     for (int i = threadIdx.x; i < (1 << kLmax); i += blockDim.x) tab[i] = table[i];
     __syncthreads();
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -39,31 +53,46 @@ __global__ __launch_bounds__(kDWaves * kWave) void exp_decode_kernel(const uint3
     const __amdgpu_buffer_rsrc_t ws = make_rsrc(words, 4u * nwords);
     uint32_t wi = k >> 5, off = k & 31;
     uint64_t buf = ((uint64_t)buf_load_u32(ws, 4u * wi) << 32) | buf_load_u32(ws, 4u * (wi + 1));
-    uint32_t nxt = buf_load_u32(ws, 4u * (wi + 2));   // the next word, loaded one refill ahead
+    // the 13 words from wi + 2: what the first chunk shifts in
+    uint32_t nx[kWin];
+    auto load_win = [&](uint32_t from) {
+#pragma unroll
+        for (int a = 0; a < kWin; ++a) nx[a] = buf_load_u32(ws, 4u * (from + a));
+    };
+    auto stage_win = [&](int slot) {
+#pragma unroll
+        for (int a = 0; a < kWin; ++a) win[wave][slot][a][lane] = nx[a];
+    };
+    load_win(wi + 2);
+    stage_win(0);
+    uint32_t cbase = wi + 2;   // stream word at position 0 of the current slot
     const uint8_t* lp = lo + base + lane;
     uint16_t* op = out + base + lane;
-    // one step: look the symbol up and advance, refilling the window from
-    // the word loaded at the previous refill; the weights of a chunk of 16
-    // steps are stored together at its end, so a wait for a stream word
-    // covers at most the previous chunk's stores.
-    constexpr int kC = 16;
-    auto step = [&]() -> uint32_t {
-        const uint32_t e = tab[(uint32_t)((buf << off) >> (64 - kLmax))];
-        off += e >> 8;
-        if (off >= 32) {
-            off -= 32;
-            ++wi;
-            buf = (buf << 32) | nxt;
-            nxt = buf_load_u32(ws, 4u * (wi + 2));
-        }
-        return (e & 0xFFu) << 8;
-    };
-    for (int j0 = 0; j0 < sg; j0 += kC) {
+    for (int j0 = 0, c = 0; j0 < sg; j0 += kC, c ^= 1) {
+        // the next chunk's window goes out first, then this chunk's low bytes;
+        // after the steps the window is staged (its loads precede the low
+        // bytes', so that wait leaves them in flight) and only then the
+        // weights are stored, so no wait ever covers a store
+        const uint32_t nbase = wi + 2;
+        load_win(nbase);
         uint32_t lv[kC], hv[kC];   // raw low bytes (indices past sg repeat the last), decoded high bytes
 #pragma unroll
         for (int u = 0; u < kC; ++u) lv[u] = lp[(size_t)kWave * min(j0 + u, sg - 1)];
 #pragma unroll
-        for (int u = 0; u < kC; ++u) hv[u] = step();   // steps past sg decode what follows the block
+        for (int u = 0; u < kC; ++u) {   // steps past sg decode what follows the block
+            const uint32_t e = tab[(uint32_t)((buf << off) >> (64 - kLmax))];
+            off += e >> 8;
+            if (off >= 32) {
+                off -= 32;
+                // at most six refills per chunk keep the index below 12 for any
+                // code of at most 12 bits; the clamp bounds a malformed table
+                buf = (buf << 32) | win[wave][c][min(wi + 2 - cbase, (uint32_t)kWin - 1)][lane];
+                ++wi;
+            }
+            hv[u] = (e & 0xFFu) << 8;
+        }
+        stage_win(c ^ 1);
+        cbase = nbase;
         if (j0 + kC <= sg) {   // uniform over the wave
 #pragma unroll
             for (int u = 0; u < kC; ++u) op[(size_t)kWave * (j0 + u)] = (uint16_t)(hv[u] | lv[u]);
