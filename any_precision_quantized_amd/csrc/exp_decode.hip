@@ -63,43 +63,68 @@ __global__ __launch_bounds__(kDWaves * kWave) void exp_decode_kernel(const uint3
 #pragma unroll
         for (int a = 0; a < kWin; ++a) win[wave][slot][a][lane] = nx[a];
     };
+    const uint8_t* lp = lo + base + lane;
+    uint16_t* op = out + base + lane;
+    uint32_t lv[kC];   // raw low bytes of the current chunk (indices past sg repeat the last)
+    auto load_lo = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < kC; ++u) lv[u] = lp[(size_t)kWave * min(j0 + u, sg - 1)];
+    };
+    // software pipeline over chunks: chunk c decodes from LDS slot c % 2; at
+    // its end the window for chunk c + 1 (loaded a chunk earlier) is staged
+    // and chunk c's weights are formed, then the loads for chunk c + 1's low
+    // bytes and chunk c + 2's window go out, and last chunk c's weights are
+    // stored, so every wait is for operations issued a chunk earlier
     load_win(wi + 2);
     stage_win(0);
     uint32_t cbase = wi + 2;   // stream word at position 0 of the current slot
-    const uint8_t* lp = lo + base + lane;
-    uint16_t* op = out + base + lane;
+    load_win(wi + 2);          // chunk 1 moves at most six words on: this window covers it
+    uint32_t nbase = wi + 2;
+    load_lo(0);
     for (int j0 = 0, c = 0; j0 < sg; j0 += kC, c ^= 1) {
-        // the next chunk's window goes out first, then this chunk's low bytes;
-        // after the steps the window is staged (its loads precede the low
-        // bytes', so that wait leaves them in flight) and only then the
-        // weights are stored, so no wait ever covers a store
-        const uint32_t nbase = wi + 2;
-        load_win(nbase);
-        uint32_t lv[kC], hv[kC];   // raw low bytes (indices past sg repeat the last), decoded high bytes
-#pragma unroll
-        for (int u = 0; u < kC; ++u) lv[u] = lp[(size_t)kWave * min(j0 + u, sg - 1)];
+        uint32_t hv[kC];   // decoded high bytes
+        // nw is the word a refill would shift in (stream word wi + 2), read
+        // from LDS at the end of every step for the next one: that read and
+        // the next step's table lookup go out together, so a step waits for
+        // one LDS round trip, not two.  The read is volatile so that it is not
+        // sunk into the refill branch.  At most six refills per chunk keep the
+        // index below 12 for any code of at most 12 bits; the clamp bounds a
+        // malformed table.
+        typedef __attribute__((address_space(3))) const volatile uint32_t lds_vu32;
+        lds_vu32* wv = (lds_vu32*)&win[wave][c][0][lane];
+        uint32_t nw = wv[min(wi + 2 - cbase, (uint32_t)kWin - 1) * kWave];
 #pragma unroll
         for (int u = 0; u < kC; ++u) {   // steps past sg decode what follows the block
             const uint32_t e = tab[(uint32_t)((buf << off) >> (64 - kLmax))];
             off += e >> 8;
             if (off >= 32) {
                 off -= 32;
-                // at most six refills per chunk keep the index below 12 for any
-                // code of at most 12 bits; the clamp bounds a malformed table
-                buf = (buf << 32) | win[wave][c][min(wi + 2 - cbase, (uint32_t)kWin - 1)][lane];
+                buf = (buf << 32) | nw;
                 ++wi;
             }
+            nw = wv[min(wi + 2 - cbase, (uint32_t)kWin - 1) * kWave];
             hv[u] = (e & 0xFFu) << 8;
         }
+        // nothing after the steps moves into them: every wait below is for
+        // memory operations issued a chunk ago, and the new loads go out only
+        // after those waits
+        __builtin_amdgcn_sched_barrier(0);
         stage_win(c ^ 1);
+        uint32_t w[kC];
+#pragma unroll
+        for (int u = 0; u < kC; ++u) w[u] = hv[u] | lv[u];
+        __builtin_amdgcn_sched_barrier(0);
         cbase = nbase;
+        nbase = wi + 2;
+        load_win(nbase);
+        load_lo(j0 + kC);
         if (j0 + kC <= sg) {   // uniform over the wave
 #pragma unroll
-            for (int u = 0; u < kC; ++u) op[(size_t)kWave * (j0 + u)] = (uint16_t)(hv[u] | lv[u]);
+            for (int u = 0; u < kC; ++u) op[(size_t)kWave * (j0 + u)] = (uint16_t)w[u];
         } else {
 #pragma unroll
             for (int u = 0; u < kC; ++u)
-                if (j0 + u < sg) op[(size_t)kWave * (j0 + u)] = (uint16_t)(hv[u] | lv[u]);
+                if (j0 + u < sg) op[(size_t)kWave * (j0 + u)] = (uint16_t)w[u];
         }
     }
 }
