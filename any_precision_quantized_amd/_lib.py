@@ -76,6 +76,7 @@ def _lib():
             "apmoe_exp_plan": [_vp, _u64, _vp, _vp, _vp],
             "apmoe_exp_encode": [_vp, _u64, _vp, _vp, _u64, _vp, _vp, _vp],
             "apmoe_exp_decode": [_vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp],
+            "apmoe_exp_decode_batch": [_c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -480,3 +481,26 @@ def exp_decode(words, block_off, lo, table, out, stream=None):
                                  _ptr(table, torch.int16, 4096, "table"), n, _ptr(out, torch.int16, n, "out"),
                                  _stream(stream))
     _check(rc, "apmoe_exp_decode")
+
+
+EXP_MAX_BATCH = 16
+
+
+def exp_decode_batch(streams, stream=None):
+    """One launch over several coded matrices: streams is a list of dicts with
+    the device tensors words, block_off, lo, table and out, as exp_decode takes."""
+    torch = _torch()
+    c = len(streams)
+    if not 1 <= c <= EXP_MAX_BATCH:
+        raise ValueError(f"1..{EXP_MAX_BATCH} matrices per call, got {c}")
+    vp = ctypes.c_void_p * c
+    u64 = ctypes.c_uint64 * c
+    words = vp(*[_ptr(d["words"], torch.int32, 2, "words") for d in streams])
+    nwords = u64(*[d["words"].numel() for d in streams])
+    boff = vp(*[_ptr(d["block_off"], torch.int32, None, "block_off") for d in streams])
+    lo = vp(*[_ptr(d["lo"], torch.uint8, d["out"].numel(), "lo") for d in streams])
+    tab = vp(*[_ptr(d["table"], torch.int16, 4096, "table") for d in streams])
+    n = u64(*[d["out"].numel() for d in streams])
+    out = vp(*[_ptr(d["out"], torch.int16, d["out"].numel(), "out") for d in streams])
+    rc = _lib().apmoe_exp_decode_batch(c, words, nwords, boff, lo, tab, n, out, _stream(stream))
+    _check(rc, "apmoe_exp_decode_batch")

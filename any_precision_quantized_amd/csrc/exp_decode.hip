@@ -34,18 +34,38 @@ constexpr int kC = 16;        // steps per chunk
 constexpr int kWin = 13;      // words staged per chunk
 constexpr int kWinPad = 16;   // LDS words per lane and slot
 
-__global__ __launch_bounds__(kDWaves * kWave) void exp_decode_kernel(const uint32_t* __restrict__ words,
-                                                                     uint32_t nwords,
-                                                                     const uint32_t* __restrict__ block_off,
-                                                                     const uint8_t* __restrict__ lo,
-                                                                     const uint16_t* __restrict__ table, uint64_t n,
-                                                                     uint16_t* __restrict__ out) {
+// Up to kMaxStreams matrices per launch, passed by value: matrix m owns the
+// workgroups [first[m], first[m + 1]).
+constexpr int kMaxStreams = APMOE_EXP_MAX_BATCH;
+struct DecodeBatch {
+    const uint32_t* words[kMaxStreams];
+    const uint32_t* block_off[kMaxStreams];
+    const uint8_t* lo[kMaxStreams];
+    const uint16_t* table[kMaxStreams];
+    uint16_t* out[kMaxStreams];
+    uint64_t n[kMaxStreams];
+    uint32_t nwords[kMaxStreams];
+    uint32_t first[kMaxStreams + 1];
+    int count;
+};
+
+__global__ __launch_bounds__(kDWaves * kWave) void exp_decode_kernel(const DecodeBatch bt) {
+    int m = 0;   // the matrix of this workgroup (uniform)
+    while (m + 1 < bt.count && blockIdx.x >= bt.first[m + 1]) ++m;
+    const uint32_t* __restrict__ words = bt.words[m];
+    const uint32_t nwords = bt.nwords[m];
+    const uint32_t* __restrict__ block_off = bt.block_off[m];
+    const uint8_t* __restrict__ lo = bt.lo[m];
+    const uint16_t* __restrict__ table = bt.table[m];
+    const uint64_t n = bt.n[m];
+    uint16_t* __restrict__ out = bt.out[m];
+    const uint32_t wg = blockIdx.x - bt.first[m];
     __shared__ uint16_t tab[1 << kLmax];
     __shared__ uint32_t win[kDWaves][2][kWinPad][kWave];   // [wave][slot][word][lane]: lanes on distinct banks
     for (int i = threadIdx.x; i < (1 << kLmax); i += blockDim.x) tab[i] = table[i];
     __syncthreads();
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const uint64_t g = (uint64_t)blockIdx.x * kDWaves + wave;
+    const uint64_t g = (uint64_t)wg * kDWaves + wave;
     const uint64_t base = g * kGroup;
     if (base >= n) return;   // uniform over the wave; no barrier follows
     const int sg = (int)min<uint64_t>(kS, (n - base) / kWave);
@@ -134,15 +154,48 @@ __global__ __launch_bounds__(kDWaves * kWave) void exp_decode_kernel(const uint3
 
 using namespace apmoe;
 
-extern "C" int apmoe_exp_decode(const uint32_t* words, uint64_t nwords, const uint32_t* block_off, const uint8_t* lo,
-                                const uint16_t* table, uint64_t n, uint16_t* out, void* stream) {
+namespace {
+int check_stream(const uint32_t* words, uint64_t nwords, const uint32_t* block_off, const uint8_t* lo,
+                 const uint16_t* table, uint64_t n, const uint16_t* out, uint64_t& wgs) {
     if (!words || !block_off || !lo || !table || !out) return APMOE_EINVAL;
     if (n == 0 || n % kWave || nwords < 2 || nwords >= (1ull << 30)) return APMOE_EINVAL;
     const uint64_t groups = (n + kGroup - 1) / kGroup;
-    const uint64_t wgs = (groups + kDWaves - 1) / kDWaves;
-    if (wgs > 0x7FFFFFFFull) return APMOE_EINVAL;
+    wgs = (groups + kDWaves - 1) / kDWaves;
+    return APMOE_OK;
+}
+}  // namespace
+
+extern "C" int apmoe_exp_decode_batch(int count, const uint32_t* const* words, const uint64_t* nwords,
+                                      const uint32_t* const* block_off, const uint8_t* const* lo,
+                                      const uint16_t* const* table, const uint64_t* n, uint16_t* const* out,
+                                      void* stream) {
+    if (count < 1 || count > kMaxStreams || !words || !nwords || !block_off || !lo || !table || !n || !out)
+        return APMOE_EINVAL;
+    DecodeBatch bt = {};
+    bt.count = count;
+    uint64_t total = 0;
+    for (int m = 0; m < count; ++m) {
+        uint64_t wgs = 0;
+        const int rc = check_stream(words[m], nwords[m], block_off[m], lo[m], table[m], n[m], out[m], wgs);
+        if (rc != APMOE_OK) return rc;
+        bt.words[m] = words[m];
+        bt.nwords[m] = (uint32_t)nwords[m];
+        bt.block_off[m] = block_off[m];
+        bt.lo[m] = lo[m];
+        bt.table[m] = table[m];
+        bt.n[m] = n[m];
+        bt.out[m] = out[m];
+        bt.first[m] = (uint32_t)total;
+        total += wgs;
+        if (total > 0x7FFFFFFFull) return APMOE_EINVAL;
+    }
+    bt.first[count] = (uint32_t)total;
     clear_stale_error();
-    hipLaunchKernelGGL(exp_decode_kernel, dim3((unsigned)wgs), dim3(kDWaves * kWave), 0, as_stream(stream), words,
-                       (uint32_t)nwords, block_off, lo, table, n, out);
+    hipLaunchKernelGGL(exp_decode_kernel, dim3((unsigned)total), dim3(kDWaves * kWave), 0, as_stream(stream), bt);
     return launch_status();
+}
+
+extern "C" int apmoe_exp_decode(const uint32_t* words, uint64_t nwords, const uint32_t* block_off, const uint8_t* lo,
+                                const uint16_t* table, uint64_t n, uint16_t* out, void* stream) {
+    return apmoe_exp_decode_batch(1, &words, &nwords, &block_off, &lo, &table, &n, &out, stream);
 }

@@ -243,7 +243,8 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
 def codec_probe(inp, reps=5):
     """Lossless exponent codec on the layer's fp16 weights (the shared expert,
     else the routed experts at 16 bits): host encode time, coded size, and
-    the GPU decode of all of them timed with events on the current stream."""
+    the GPU decode of all of them (one batched launch) timed with events on
+    the current stream."""
     import numpy as np
     import torch
     from any_precision_quantized_amd import _lib
@@ -269,9 +270,9 @@ def codec_probe(inp, reps=5):
         dev.append(d)
     stream = torch.cuda.current_stream()
 
-    def run():
-        for d in dev:
-            _lib.exp_decode(d["words"], d["block_off"], d["lo"], d["table"], d["out"])
+    def run():   # every matrix in one launch (a matrix alone leaves most of the GPU idle)
+        for i in range(0, len(dev), _lib.EXP_MAX_BATCH):
+            _lib.exp_decode_batch(dev[i:i + _lib.EXP_MAX_BATCH])
 
     run()
     torch.cuda.synchronize()

@@ -452,6 +452,19 @@ int apmoe_exp_encode(const uint16_t* w, uint64_t n, const uint8_t* lengths, uint
 int apmoe_exp_decode(const uint32_t* words, uint64_t nwords, const uint32_t* block_off, const uint8_t* lo,
                      const uint16_t* table, uint64_t n, uint16_t* out, void* stream);
 
+/* Up to APMOE_EXP_MAX_BATCH coded matrices decoded by one launch (the same
+ * passage: a layer's fp16 weights are decoded together once they are in GPU
+ * memory).  Host arrays of count entries, each entry as apmoe_exp_decode's
+ * arguments (device pointers, each matrix with its own table); every entry
+ * is validated before anything is launched.  A small matrix alone gives the
+ * GPU less than one decoding wave per SIMD, and each wave's time is one
+ * block's chain of dependent lookups, so decoding a layer's matrices
+ * together takes about as long as decoding one of them. */
+#define APMOE_EXP_MAX_BATCH 16
+int apmoe_exp_decode_batch(int count, const uint32_t* const* words, const uint64_t* nwords,
+                           const uint32_t* const* block_off, const uint8_t* const* lo, const uint16_t* const* table,
+                           const uint64_t* n, uint16_t* const* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

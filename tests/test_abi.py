@@ -15,7 +15,7 @@ from oracle import planner as planner_ref
 def test_library_exports_header_symbols():
     lib = _lib._lib()
     names = _lib.header_symbols()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout

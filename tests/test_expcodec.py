@@ -145,3 +145,11 @@ def test_native_encoder_argument_errors():
     assert lib.apmoe_exp_encode(w.ctypes.data, 128, bad.ctypes.data, words.ctypes.data, nw.value, *args) == _lib.EINVAL
     assert lib.apmoe_exp_encode(w.ctypes.data, 128, lengths.ctypes.data, words.ctypes.data, nw.value, *args) == _lib.OK
     assert lib.apmoe_exp_decode(None, 6, None, None, None, 128, None, None) == _lib.EINVAL
+    # batched decode: count out of range, missing arrays, one bad entry
+    vp2 = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    u2 = (ctypes.c_uint64 * 2)(6, 6)
+    n2 = (ctypes.c_uint64 * 2)(128, 100)         # 100 is not a multiple of 64
+    assert lib.apmoe_exp_decode_batch(0, vp2, u2, vp2, vp2, vp2, n2, vp2, None) == _lib.EINVAL
+    assert lib.apmoe_exp_decode_batch(_lib.EXP_MAX_BATCH + 1, vp2, u2, vp2, vp2, vp2, n2, vp2, None) == _lib.EINVAL
+    assert lib.apmoe_exp_decode_batch(2, None, u2, vp2, vp2, vp2, n2, vp2, None) == _lib.EINVAL
+    assert lib.apmoe_exp_decode_batch(2, vp2, u2, vp2, vp2, vp2, n2, vp2, None) == _lib.EINVAL

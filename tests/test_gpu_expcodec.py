@@ -65,3 +65,24 @@ def test_decode_full_size_fp16_weights(name, which):
         assert torch.equal(out, ref), mname
         G.say(f"  {mname}: {w.size} weights, {enc['words'].size * 4 + w.size + enc['block_off'].size * 4} "
               f"bytes coded of {2 * w.size}")
+
+
+def test_decode_batch_matches_each_matrix():
+    """One launch over several coded matrices of different sizes, each with its
+    own table (ragged last groups included), equals the weights bit for bit;
+    the workgroups of one matrix never write another's output."""
+    import torch
+    G.say("exp decode batch")
+    rng = np.random.default_rng(11)
+    sizes = [64, 64 * 256 * 5 + 64 * 3, 64 * 256, 64 * 77]
+    ws, streams = [], []
+    for i, n in enumerate(sizes):
+        w = rng.normal(0.0, 0.02 * (i + 1), n).astype(np.float16).view(np.uint16)
+        d = _device(_lib.exp_encode(w))
+        d["out"] = torch.full((n,), -1, dtype=torch.int16, device="cuda")
+        ws.append(w)
+        streams.append(d)
+    _lib.exp_decode_batch(streams)
+    torch.cuda.synchronize()
+    for w, d in zip(ws, streams):
+        assert np.array_equal(d["out"].cpu().numpy().view(np.uint16), w)
