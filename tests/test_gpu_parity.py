@@ -47,6 +47,10 @@ SMALL = {
     # the same with a long down projection (K = 7168, 56 steps): 64-token
     # passes under a K split
     "mid_groups_ksplit": synth.custom("mid_groups_ksplit", E=2, H=128, I=7168, k=1, T=90, bits=(3, 5)),
+    # 40 experts (three 16-expert router tiles) over H = 1024 split in two
+    # hidden chunks: partial logits added by the select launch
+    "router_tiles": synth.custom("router_tiles", E=40, H=1024, I=128, k=4, T=48,
+                                 bits=tuple((5, 3, 6, 4)[e % 4] for e in range(40))),
     # the largest expert count (256): router lanes hold four experts, the item
     # lookups scan four chunks of 64 experts
     "max_experts": synth.custom("max_experts", E=256, H=64, I=96, k=8, T=48,
@@ -241,6 +245,7 @@ GRAPH_CASES = {
     "tiny": SMALL["tiny"],                  # one-kernel router
     "shared_fused": SMALL["shared_fused"],  # always-on fp16 experts: tile path at mfma_min 16
     "ragged": SMALL["ragged"],
+    "router_tiles": SMALL["router_tiles"],  # matrix-core logits + select launch
     # one token over two experts, down stage K = 7168 (56 steps): the down GEMV
     # splits K in two and runs its finalize kernel
     "ksplit": synth.custom("ksplit", E=2, H=128, I=7168, k=1, T=1, bits=(5, 3)),
