@@ -94,6 +94,12 @@ __global__ __launch_bounds__(kRtWaves * kWave) void logits_kernel(
     const int slices = KC * kRtWaves, slice = kc * kRtWaves + wave;
     const int u0 = (int)((long long)slice * U / slices), u1 = (int)((long long)(slice + 1) * U / slices);
     const bool nrm = norms && et == 0;   // uniform over the workgroup
+    // the biases the in-place selection adds (ET * KC == 1), loaded now so
+    // that no load waits at the end (clamped index, no per-lane condition)
+    constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
+    float bv[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) bv[c] = (bias && ET * KC == 1) ? bias[min(lane + kWave * c, E - 1)] : 0.f;
     // rows past T or E read a valid row; their sums are never used
     const half_t* xr = x + (size_t)min(t0 + r, T - 1) * H + 8 * g;
     const float* wr = w_router + (size_t)min(e0 + r, E - 1) * H + 8 * g;
@@ -158,13 +164,12 @@ __global__ __launch_bounds__(kRtWaves * kWave) void logits_kernel(
     __syncthreads();
     const int t = t0 + wave;
     if (t >= T) return;   // uniform over the wave; no barrier follows
-    constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
     double* row = L + wave * Ep;
     double v[kPer];
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         const int e = lane + kWave * c;
-        v[c] = e < E ? (double)scale * (row[e] + (bias ? (double)bias[e] : 0.0)) : -__builtin_inf();
+        v[c] = e < E ? (double)scale * (row[e] + (double)bv[c]) : -__builtin_inf();
     }
     // the row is this wave's alone from here: its first k entries take the chosen logits
     select_topk<kPer>(v, E, k, t, lane, row, topk_ids, topk_w);
@@ -285,16 +290,21 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
     if (t >= T) return;   // uniform over the wave; no block barrier follows
     const int tt = t / kRt, tr = t % kRt, Ep = ET * kRt;
     const double* p0 = part + ((size_t)tt * KC * kRt + tr) * Ep;
+    // the first 64 norm partials (lane q: chunk q) go out with the logits'
+    // loads, so the norm adds no second memory round trip
+    const float pv0 = (norms && lane < KC) ? npart[((size_t)tt * KC + lane) * kRt + tr] : 0.f;
     constexpr int kPer = APMOE_MAX_EXPERTS / kWave;
     // each logit adds its KC partials in chunk order; the loads carry no
     // condition (columns past Ep re-read column Ep - 1, never used), so the
     // compiler issues a whole unrolled group of them before the first add
     double v[kPer];
     int ec[kPer];
+    float bv[kPer];   // biases, loaded with the partials (clamped index, no per-lane condition)
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         v[c] = 0.0;
         ec[c] = min(lane + kWave * c, Ep - 1);
+        bv[c] = bias ? bias[min(lane + kWave * c, E - 1)] : 0.f;
     }
     constexpr int kQB = 4;   // chunks whose loads go out together
     for (int q0 = 0; q0 < KC; q0 += kQB) {
@@ -314,13 +324,13 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(const double*
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         const int e = lane + kWave * c;
-        v[c] = e < E ? (double)scale * (v[c] + (bias ? (double)bias[e] : 0.0)) : -__builtin_inf();
+        v[c] = e < E ? (double)scale * (v[c] + (double)bv[c]) : -__builtin_inf();
     }
     if (norms) {   // lane q loads chunk q's partial; the wave adds them in chunk order
         float sm = 0.f;
         for (int q0 = 0; q0 < KC; q0 += kWave) {
             const int q = q0 + lane;
-            const float pv = q < KC ? npart[((size_t)tt * KC + q) * kRt + tr] : 0.f;
+            const float pv = q0 == 0 ? pv0 : (q < KC ? npart[((size_t)tt * KC + q) * kRt + tr] : 0.f);
             const int n = min(kWave, KC - q0);
             for (int j = 0; j < n; ++j)
                 sm += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), j));

@@ -445,17 +445,31 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
             if rc != 0:
                 raise _lib.ApmoeError(rc, "route + permute")
 
-        pair_us = {}
-        for stats in (False, True, False, True):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(probe_steps)]
-            for i in range(probe_steps):
-                evs[i][0].record(stream)
+        # each variant captured as a HIP graph of n back-to-back pairs (the way
+        # the step runs), replayed in alternation with the other
+        n = 50
+        graphs = {}
+        for stats in (False, True):
+            for _ in range(3):
                 pair(stats)
-                evs[i][1].record(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                sp = torch.cuda.current_stream().cuda_stream
+                for _ in range(n):
+                    pair(stats)
+            graphs[stats] = g
+        sp = stream.cuda_stream
+        torch.cuda.synchronize()
+        pair_us = {}
+        for stats in (False, True) * 4:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graphs[stats].replay()
+            e1.record(stream)
             torch.cuda.synchronize()
-            pair_us.setdefault(stats, []).append(sum(a.elapsed_time(b) for a, b in evs) / probe_steps * 1e3)
-        route_stats_in_step_us = float(np.mean(pair_us[True]) - np.mean(pair_us[False]))
+            pair_us.setdefault(stats, []).append(e0.elapsed_time(e1) * 1e3 / n)
+        del graphs
+        route_stats_in_step_us = float(np.median(pair_us[True]) - np.median(pair_us[False]))
 
     # Timed region: K whole steps; the dominant launch is bracketed by events.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
