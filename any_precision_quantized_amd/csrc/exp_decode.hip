@@ -2,7 +2,7 @@
 //
 // One wave per group of 64 blocks, lane l decoding block l: each step peeks
 // 12 bits of the lane's stream, looks the symbol and its code length up in a
-// 4096-entry table in LDS, and writes weight g * 16384 + 64 j + l = (symbol
+// 4096-entry table in LDS, and writes weight g * 9216 + 64 j + l = (symbol
 // << 8) | its raw low byte, so every store of the wave covers 64 consecutive
 // weights (128 bytes) and every low-byte load 64 consecutive bytes.  A lane
 // keeps a 64-bit window of its stream and shifts in one 32-bit word whenever
@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kDWaves = 4;
 constexpr int kLmax = 12;
-constexpr int kS = 256;
+constexpr int kS = 144;   // symbols per block (the stream format's block length)
 constexpr int kGroup = kWave * kS;
 constexpr int kC = 16;        // steps per chunk
 constexpr int kWin = 13;      // words staged per chunk

@@ -21,7 +21,7 @@ Readings taken here (the page gives no format):
     every non-zero count is raised to at least total >> (12 - r) for
     r = 2, 3, ... (the first r that makes the code fit) and the code is
     rebuilt.  Codes are canonical: by (length, symbol), consecutive values;
-  * layout: weights are taken in groups of 64 * S (S = 256); block (g, l),
+  * layout: weights are taken in groups of 64 * S (S = 144); block (g, l),
     l = 0..63, holds the weights g*64*S + 64*j + l for j = 0..S_g - 1, with
     S_g = min(S, (n - g*64*S) / 64) (n a multiple of 64).  The bit stream is
     the blocks' codes in block order, each block's codes in j order, most
@@ -37,7 +37,7 @@ import numpy as np
 
 NSYM = 256
 LMAX = 12
-S = 256          # symbols per block
+S = 144          # symbols per block
 LANES = 64       # blocks per group
 
 

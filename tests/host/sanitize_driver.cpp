@@ -25,6 +25,10 @@
 
 using Rng = std::mt19937_64;
 
+// the exponent stream format: groups of 64 blocks of up to kBlockSyms symbols
+constexpr uint64_t kBlockSyms = 144;
+constexpr uint64_t kGroupW = 64 * kBlockSyms;
+
 static uint64_t uni(Rng& r, uint64_t lo, uint64_t hi) { return std::uniform_int_distribution<uint64_t>(lo, hi)(r); }
 
 // Arena against a shadow map of 256-byte units.
@@ -231,9 +235,9 @@ static int codec_fuzz(Rng& rng) {
         for (uint64_t blk = 0; blk < nblocks; ++blk) {
             const uint64_t g = blk / 64, l = blk % 64;
             uint64_t pos = off[blk];
-            for (uint64_t j = 0; j < 256; ++j) {
-                const uint64_t i = g * 16384 + 64 * j + l;
-                if (64 * j >= std::min<uint64_t>(16384, n - g * 16384)) break;
+            for (uint64_t j = 0; j < kBlockSyms; ++j) {
+                const uint64_t i = g * kGroupW + 64 * j + l;
+                if (64 * j >= std::min<uint64_t>(kGroupW, n - g * kGroupW)) break;
                 CHECK(pos / 32 + 1 < nwords);
                 const uint64_t pair = ((uint64_t)words[pos / 32] << 32) | words[pos / 32 + 1];
                 const uint32_t peek = (uint32_t)((pair << (pos % 32)) >> 52);

@@ -70,14 +70,14 @@ def test_length_limit_on_fibonacci_counts():
     assert np.array_equal(X.decode(lengths, words, offs, lo, w.size), w)
 
 
-@pytest.mark.parametrize("n", [64, 64 * 256, 64 * 256 + 64 * 37])
+@pytest.mark.parametrize("n", [64, 64 * X.S, 64 * X.S + 64 * 37])
 def test_round_trip_fp16_weights(n):
     rng = np.random.default_rng(n)
     w = rng.normal(0.0, 0.02, n).astype(np.float16).view(np.uint16)
     lengths, words, offs, lo = X.encode(w)
-    assert offs.size == 64 * (-(-n // (64 * 256)))
+    assert offs.size == 64 * (-(-n // (64 * X.S)))
     assert np.array_equal(X.decode(lengths, words, offs, lo, n), w)
-    if n >= 64 * 256:
+    if n >= 64 * X.S:
         # N(0, 0.02) weights: the high byte carries ~5.5 bits of information
         coded = X.coded_bits(lengths, X.histogram(w >> 8))
         assert coded / n < 6.5
@@ -108,9 +108,9 @@ def _native_vs_oracle(w):
 def test_native_encoder_matches_oracle(case):
     rng = np.random.default_rng(11)
     if case == "normal":
-        w = rng.normal(0.0, 0.02, 64 * 256 * 2).astype(np.float16).view(np.uint16)
+        w = rng.normal(0.0, 0.02, 64 * X.S * 2).astype(np.float16).view(np.uint16)
     elif case == "partial_group":
-        w = rng.normal(0.0, 1.0, 64 * 256 + 64 * 5).astype(np.float16).view(np.uint16)
+        w = rng.normal(0.0, 1.0, 64 * X.S + 64 * 5).astype(np.float16).view(np.uint16)
     elif case == "one_symbol":
         w = (np.full(64 * 9, 0x3C00, np.uint16) | rng.integers(0, 256, 64 * 9).astype(np.uint16))
     else:

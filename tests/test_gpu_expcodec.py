@@ -31,7 +31,7 @@ def _decode(enc, n):
     return out
 
 
-@pytest.mark.parametrize("n", [64, 64 * 256, 64 * 256 * 3 + 64 * 17])
+@pytest.mark.parametrize("n", [64, 64 * X.S, 64 * X.S * 3 + 64 * 17])
 def test_decode_native_stream(n):
     G.say(f"exp decode n={n}")
     rng = np.random.default_rng(n + 1)
@@ -41,7 +41,7 @@ def test_decode_native_stream(n):
 
 
 def test_decode_oracle_stream():
-    n = 64 * 256 + 64 * 3
+    n = 64 * X.S + 64 * 3
     rng = np.random.default_rng(3)
     w = rng.normal(0.0, 1.0, n).astype(np.float16).view(np.uint16)
     lengths, words, offs, lo = X.encode(w)
@@ -74,7 +74,7 @@ def test_decode_batch_matches_each_matrix():
     import torch
     G.say("exp decode batch")
     rng = np.random.default_rng(11)
-    sizes = [64, 64 * 256 * 5 + 64 * 3, 64 * 256, 64 * 77]
+    sizes = [64, 64 * X.S * 5 + 64 * 3, 64 * X.S, 64 * 77]
     ws, streams = [], []
     for i, n in enumerate(sizes):
         w = rng.normal(0.0, 0.02 * (i + 1), n).astype(np.float16).view(np.uint16)
