@@ -243,8 +243,8 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
 def codec_probe(inp, reps=5):
     """Lossless exponent codec on the layer's fp16 weights (the shared expert,
     else the routed experts at 16 bits): host encode time, coded size, and
-    the GPU decode of all of them (one batched launch) timed with events on
-    the current stream."""
+    the GPU decode of all of them (one batched launch, `reps` of them replayed
+    from a HIP graph) timed with events on the current stream."""
     import numpy as np
     import torch
     from any_precision_quantized_amd import _lib
@@ -280,13 +280,22 @@ def codec_probe(inp, reps=5):
         ref = torch.from_numpy(np.ascontiguousarray(m).view(np.int16).reshape(-1)).cuda()
         if not torch.equal(d["out"], ref):
             raise RuntimeError("exponent codec: decode differs from the weights")
+    # the decodes replayed from a HIP graph: launched one by one from Python,
+    # the host takes longer per call than a small decode takes on the GPU
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            run()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(reps):
-        run()
+    g.replay()
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3
+    del g
     raw = sum(2 * enc["n"] for enc in encs)
     coded = sum(4 * enc["words"].size + enc["lo"].size + 4 * enc["block_off"].size + 2 * 4096 for enc in encs)
     moved = coded + raw                       # read the coded form, write the weights
@@ -668,7 +677,7 @@ def main():
     if not args.no_paging_probe:
         result["paging"] = paging_probe(cfg, inp, bits, mfma_min)
     if not args.no_codec_probe:
-        result["exp_codec"] = codec_probe(inp)
+        result["exp_codec"] = codec_probe(inp, reps=10)
     result["planner"] = planner_probe(inp)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, bits)
