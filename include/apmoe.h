@@ -431,8 +431,8 @@ int apmoe_pager_destroy(apmoe_pager* pager);
  * id), leaves id = symbol, merged nodes 256, 257, ... in creation order),
  * lengths limited to 12 bits by raising every non-zero count to at least
  * total >> (12 - r), r = 2, 3, ..., until the code fits; the low byte is kept
- * raw.  Weights go in groups of 16384: block l (0..63) of group g holds
- * weights g*16384 + 64j + l, j = 0..min(256, (n - g*16384)/64) - 1; the bit
+ * raw.  Weights go in groups of 9216: block l (0..63) of group g holds
+ * weights g*9216 + 64j + l, j = 0..min(144, (n - g*9216)/64) - 1; the bit
  * stream is the blocks' codes in block order, most significant bit first in
  * 32-bit words, ended by two zero words.
  *  plan    [host] w: n fp16 bit patterns (n > 0, n % 64 == 0, 12 n < 2^32);
