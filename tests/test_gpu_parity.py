@@ -163,7 +163,17 @@ def test_full_size_layer(name):
           f"groups {sorted(got['counts'].tolist(), reverse=True)[:8]}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen_decode", "mixtral_decode_t8", "e128_decode", "mixtral_prefill"])
+# Expert counts that give the grouping launch's per-expert sums groups of 64,
+# 32, 16, 8 and 4 lanes (a shared expert's always-on experts take none), and
+# a grouping of more slots than its LDS parks (the workspace path).
+STATS_CASES = {
+    "e24": synth.custom("e24", E=24, H=256, I=128, k=3, T=40, bits=tuple((3, 4, 5, 6)[e % 4] for e in range(24))),
+    "park_ws": synth.custom("park_ws", E=8, H=256, I=128, k=2, T=8200, bits=(3, 4, 5, 6, 3, 4, 5, 6)),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen_decode", "mixtral_decode_t8", "e128_decode", "mixtral_prefill",
+                                  "e24", "router_tiles", "max_experts", "max_experts_shared", "park_ws"])
 def test_route_stats(name):
     """Per-expert routing mass and routing-weighted input norm against the
     oracle's statistics over its own routing: as the forward computes them
@@ -171,7 +181,7 @@ def test_route_stats(name):
     router at Mixtral T = 8, the two-kernel one elsewhere) and as
     apmoe_route_stats computes them alone."""
     import torch
-    cfg = synth.get(name)
+    cfg = STATS_CASES.get(name) or SMALL.get(name) or synth.get(name)
     G.say(f"route stats {name}")
     inp = G.inputs(cfg)
     bits = resolve_bits(inp)
