@@ -91,31 +91,6 @@ __device__ inline int wave_incl_scan(int v) {
     return v;
 }
 
-// Wave-wide argmax over (value, index): the larger value, ties to the lower
-// index (a total order, so the result does not depend on the combining order).
-__device__ inline void take_max(double& v, int& e, double ov, int oe) {
-    if (ov > v || (ov == v && oe < e)) {
-        v = ov;
-        e = oe;
-    }
-}
-template <int C>
-__device__ inline void argmax_step(double& v, int& e) {
-    take_max(v, e, dpp64<C>(v), (int)dpp32<C>((uint32_t)e));
-}
-__device__ inline void wave_argmax(double& v, int& e) {
-    argmax_step<kDppQuad1032>(v, e);
-    argmax_step<kDppQuad2301>(v, e);
-    argmax_step<kDppRowHalfMirror>(v, e);
-    argmax_step<kDppRowMirror>(v, e);
-    double bv = lane_f64(v, 0);
-    int be = (int)lane_u32((uint32_t)e, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) take_max(bv, be, lane_f64(v, 16 * r), (int)lane_u32((uint32_t)e, 16 * r));
-    v = bv;
-    e = be;
-}
-
 __device__ inline float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }

@@ -38,6 +38,32 @@ constexpr int kUnit = 32;      // hidden columns per unit (four lane groups x 8)
 typedef double double4v_t __attribute__((ext_vector_type(4)));
 typedef float float4v_t __attribute__((ext_vector_type(4)));
 
+// Wave-wide argmax of (v, e), ties to the lower e, in two reductions: the
+// maximum of v (DPP within rows, then the four row results), then the lowest e
+// among the lanes that hold it.  Every lane ends with the winner.  (Given
+// each lane's own best with its lowest e, the lowest e of the lanes holding
+// the maximum is the lowest e of all the entries equal to it.)
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = fmax(v, dpp64<kDppQuad1032>(v));
+    v = fmax(v, dpp64<kDppQuad2301>(v));
+    v = fmax(v, dpp64<kDppRowHalfMirror>(v));
+    v = fmax(v, dpp64<kDppRowMirror>(v));
+    return fmax(fmax(lane_f64(v, 0), lane_f64(v, 16)), fmax(lane_f64(v, 32), lane_f64(v, 48)));
+}
+__device__ __forceinline__ int wave_min_i32(int e) {
+    e = min(e, (int)dpp32<kDppQuad1032>((uint32_t)e));
+    e = min(e, (int)dpp32<kDppQuad2301>((uint32_t)e));
+    e = min(e, (int)dpp32<kDppRowHalfMirror>((uint32_t)e));
+    e = min(e, (int)dpp32<kDppRowMirror>((uint32_t)e));
+    return min(min((int)lane_u32((uint32_t)e, 0), (int)lane_u32((uint32_t)e, 16)),
+               min((int)lane_u32((uint32_t)e, 32), (int)lane_u32((uint32_t)e, 48)));
+}
+__device__ __forceinline__ void wave_argmax(double& v, int& e) {
+    const double m = wave_max_f64(v);
+    e = wave_min_i32(v == m ? e : 0x7FFFFFFF);
+    v = m;
+}
+
 // k rounds of a wave-wide argmax over v (lane's experts lane + 64c), ties to
 // the lower expert, then the softmax over the chosen logits in fp64: lane j
 // takes the exponentials of chosen logits j, j + 64, ... and the wave adds
