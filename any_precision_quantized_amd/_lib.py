@@ -390,8 +390,8 @@ class Arena:
 class Pager:
     """apmoe_pager_*: residency of E experts' planes and LUTs in a device arena.
 
-    host_planes / host_luts: host tensors (pinned) as the C ABI describes;
-    they are kept referenced here for the pager's lifetime."""
+    host_planes / host_luts: host tensors as the C ABI describes; the pager
+    copies them into its own pinned memory when it is created."""
 
     def __init__(self, E, H, I, host_planes, host_luts, arena, desc, bits):
         torch = _torch()
@@ -399,6 +399,14 @@ class Pager:
         for t in list(host_planes) + list(host_luts):
             if t.device.type != "cpu" or not t.is_contiguous():
                 raise TypeError("host copies must be contiguous host tensors")
+        for i in range(3 * E):
+            rows, cols = (I, H) if i % 3 < 2 else (H, I)
+            if host_planes[i].numel() * host_planes[i].element_size() < 4 * packed_plane_words(rows, cols):
+                raise ValueError(f"host planes {i}: too small for a {rows} x {cols} matrix")
+            for b in range(3, 7):
+                t = host_luts[4 * i + b - 3]
+                if t.numel() * t.element_size() < rows * (1 << b) * 2:
+                    raise ValueError(f"host LUT {i}, {b} bits: too small for {rows} rows")
         self._keep = (list(host_planes), list(host_luts), arena, desc, bits)
         self.E = E
         hp = (_vp * (3 * E))(*[t.data_ptr() for t in host_planes])

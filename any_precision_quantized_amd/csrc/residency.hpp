@@ -189,6 +189,150 @@ std::vector<Block> retired_blocks(const std::vector<M>& mats) {
     return r;
 }
 
+// The pager's pinned host copy, by promotion step and then expert: the block
+// of step s = 3..6 of an expert holds what going to s bits adds (for s = 3,
+// from no planes): the new planes of gate, up and down (planes 0..2 for s = 3,
+// plane s-1 otherwise; each matrix's planes back to back), then the s-bit
+// LUTs of gate, up and down.  Raising an expert by one step is then one
+// contiguous range, and raising experts with adjacent indices to the same
+// step is one range too.
+inline int step_first_plane(int s) { return s == 3 ? 0 : s - 1; }
+inline int step_planes(int s) { return s == 3 ? 3 : 1; }
+
+template <class M>
+uint64_t step_plane_bytes(const M* m3, int s) {
+    return (uint64_t)step_planes(s) * (m3[0].slab + m3[1].slab + m3[2].slab);
+}
+
+template <class M>
+uint64_t step_lut_bytes(const M* m3, int s) {
+    return m3[0].lut_bytes[s - 3] + m3[1].lut_bytes[s - 3] + m3[2].lut_bytes[s - 3];
+}
+
+struct HostLayout {
+    std::vector<uint64_t> step_off;   // [E][4]: where step s = 3..6 of expert e starts
+    uint64_t bytes = 0;
+};
+
+// mats: 3 per expert (gate, up, down), as the pager holds them.
+template <class M>
+HostLayout host_layout(const std::vector<M>& mats) {
+    HostLayout L;
+    const size_t E = mats.size() / 3;
+    L.step_off.resize(4 * E);
+    for (int s = 3; s <= 6; ++s)
+        for (size_t e = 0; e < E; ++e) {
+            L.step_off[4 * e + s - 3] = L.bytes;
+            L.bytes += step_plane_bytes(&mats[3 * e], s) + step_lut_bytes(&mats[3 * e], s);
+        }
+    return L;
+}
+
+// Offset in the host copy of plane p of matrix j (0 gate, 1 up, 2 down) of
+// expert e, and of its b-bit LUT.
+template <class M>
+uint64_t host_plane_off(const std::vector<M>& mats, const HostLayout& L, size_t e, int j, int p) {
+    const int s = p < 3 ? 3 : p + 1;
+    uint64_t o = L.step_off[4 * e + s - 3];
+    for (int i = 0; i < j; ++i) o += (uint64_t)step_planes(s) * mats[3 * e + i].slab;
+    return o + (uint64_t)(p - step_first_plane(s)) * mats[3 * e + j].slab;
+}
+
+template <class M>
+uint64_t host_lut_off(const std::vector<M>& mats, const HostLayout& L, size_t e, int j, int b) {
+    uint64_t o = L.step_off[4 * e + b - 3] + step_plane_bytes(&mats[3 * e], b);
+    for (int i = 0; i < j; ++i) o += mats[3 * e + i].lut_bytes[b - 3];
+    return o;
+}
+
+struct Copy {
+    uint64_t dst, src, bytes;
+};
+
+// The copies that make a claimed change resident.  h2d: src is an offset
+// into the host copy, dst an arena offset; dev: copies within the arena.
+// Staged (host to a staging block at staging_off, one range per run of
+// contiguous step blocks, then placed device side): every h2d dst lies in the
+// staging block, whose size is staged_bytes.  Direct: each matrix's planes of one
+// step and each LUT go straight to their block.  Both move a relocated
+// block's resident planes device side and copy the same host bytes: the new
+// planes and the new LUT of every matrix, nothing more.  ok is false if the
+// three matrices of an expert disagree on their bitwidths (they never do in
+// the pager).  max_copy > 0 (a multiple of 256) splits every host-to-device
+// range into pieces of at most that many bytes.
+struct CopyPlan {
+    std::vector<Copy> h2d, dev;
+    uint64_t staged_bytes = 0;
+    bool ok = true;
+};
+
+template <class M>
+CopyPlan plan_copies(const std::vector<M>& mats, const HostLayout& L, bool staged, uint64_t staging_off,
+                     uint64_t max_copy = 0) {
+    CopyPlan P;
+    const size_t E = mats.size() / 3;
+    uint64_t cur = staging_off;
+    for (size_t e = 0; e < E; ++e) {
+        const M* m3 = &mats[3 * e];
+        for (int j = 1; j < 3; ++j)
+            if (m3[j].have != m3[0].have || m3[j].want != m3[0].want || m3[j].new_lut != m3[0].new_lut)
+                P.ok = false;
+        if (!P.ok) return P;
+        for (int j = 0; j < 3; ++j)
+            if (m3[j].moved && m3[j].have)
+                P.dev.push_back(Copy{m3[j].planes_new.off, m3[j].planes.off, (uint64_t)m3[j].have * m3[j].slab});
+        if (staged) continue;
+        const int have = m3[0].have, want = m3[0].want;
+        for (int s = have ? have + 1 : 3; s <= want; ++s)
+            for (int j = 0; j < 3; ++j)
+                P.h2d.push_back(Copy{m3[j].planes_new.off + (uint64_t)step_first_plane(s) * m3[j].slab,
+                                     host_plane_off(mats, L, e, j, step_first_plane(s)),
+                                     (uint64_t)step_planes(s) * m3[j].slab});
+        if (m3[0].new_lut)
+            for (int j = 0; j < 3; ++j)
+                P.h2d.push_back(Copy{m3[j].lut_new.off, host_lut_off(mats, L, e, j, want), m3[j].lut_bytes[want - 3]});
+    }
+    // staged, in host-copy order (step, then expert), so adjacent blocks merge
+    // into one range: the new planes of every step an expert climbs, and the
+    // LUTs of the step it lands on (a demotion: those LUTs alone)
+    for (int s = 3; staged && s <= 6; ++s)
+        for (size_t e = 0; e < E; ++e) {
+            const M* m3 = &mats[3 * e];
+            const int have = m3[0].have, want = m3[0].want;
+            const bool planes = want > have && s >= (have ? have + 1 : 3) && s <= want;
+            const bool luts = m3[0].new_lut && s == want;
+            if (!planes && !luts) continue;
+            const uint64_t pb = step_plane_bytes(m3, s), lb = step_lut_bytes(m3, s);
+            const uint64_t src = L.step_off[4 * e + s - 3] + (planes ? 0 : pb);
+            const uint64_t n = (planes ? pb : 0) + (luts ? lb : 0);
+            if (!P.h2d.empty() && P.h2d.back().src + P.h2d.back().bytes == src &&
+                P.h2d.back().dst + P.h2d.back().bytes == cur)
+                P.h2d.back().bytes += n;
+            else
+                P.h2d.push_back(Copy{cur, src, n});
+            uint64_t o = cur;
+            for (int j = 0; planes && j < 3; ++j) {
+                const uint64_t nb = (uint64_t)step_planes(s) * m3[j].slab;
+                P.dev.push_back(Copy{m3[j].planes_new.off + (uint64_t)step_first_plane(s) * m3[j].slab, o, nb});
+                o += nb;
+            }
+            for (int j = 0; luts && j < 3; ++j) {
+                P.dev.push_back(Copy{m3[j].lut_new.off, o, m3[j].lut_bytes[s - 3]});
+                o += m3[j].lut_bytes[s - 3];
+            }
+            cur += n;
+        }
+    P.staged_bytes = cur - staging_off;
+    if (max_copy) {
+        std::vector<Copy> split;
+        for (const Copy& c : P.h2d)
+            for (uint64_t o = 0; o < c.bytes; o += max_copy)
+                split.push_back(Copy{c.dst + o, c.src + o, std::min(max_copy, c.bytes - o)});
+        P.h2d.swap(split);
+    }
+    return P;
+}
+
 // The staged change becomes the resident state (at the commit).
 template <class M>
 void adopt(std::vector<M>& mats) {

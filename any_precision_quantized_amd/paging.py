@@ -2,7 +2,8 @@
 expert's bitwidth, moved between host and GPU by the library's pager.
 
 ``PagedExperts`` keeps a host copy of every routed expert's packed planes
-and LUTs in pinned memory and a device arena for the resident part.  Its
+and LUTs (the pager takes its own pinned copy of them when it is created) and
+a device arena for the resident part.  Its
 ``ExpertTable`` carries only the fp16 weights (for experts that may run at 16
 bits); plane and LUT pointers are written by the pager's commits.  After
 ``attach(layer)`` the layer runs on the paged weights, and ``apply(bits)``
@@ -12,10 +13,32 @@ commit run at the old bitwidths and later ones at the new.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 
 from . import _lib
 from .layer import MATS, ExpertTable
+
+
+def _hip():
+    return ctypes.CDLL("libamdhip64.so")
+
+
+def _copy_stream(device):
+    """A non-blocking stream made with HIP itself for the pager's copies.
+    HIP spreads streams over a few hardware queues and gives a new one the
+    least used; torch's pool streams are handed out round-robin, so one of
+    them lands in the queue of the default stream one time in four.  A copy
+    stream that shares the layer stream's queue was measured to slow the
+    layer's steps about twofold while the copies run."""
+    import torch
+    with torch.cuda.device(device):
+        s = ctypes.c_void_p()
+        rc = _hip().hipStreamCreateWithFlags(ctypes.byref(s), ctypes.c_uint(1))   # hipStreamNonBlocking
+        if rc != 0:
+            raise RuntimeError(f"hipStreamCreateWithFlags failed ({rc})")
+        return torch.cuda.ExternalStream(s.value, device=device)
 
 
 def arena_bytes_for(H, I, E, bits_max=6, slack=1.25):
@@ -32,7 +55,7 @@ class PagedExperts:
         """experts: per expert a mapping gate/up/down -> matrix with canonical
         ``planes`` uint32 [6, rows, cols/32], ``luts`` (four fp16 [rows, 2**b])
         and optional ``w16``.  The planes are packed once on the device (the
-        layout the kernels read) and copied to pinned host memory."""
+        layout the kernels read) and copied to host memory."""
         import torch
         self.E, self.H, self.I = len(experts), H, I
         self.device = device
@@ -46,11 +69,11 @@ class PagedExperts:
                 canon = torch.from_numpy(np.ascontiguousarray(m.planes).view(np.int32)).to(device)
                 packed = torch.empty(_lib.packed_plane_words(rows, cols), dtype=torch.int32, device=device)
                 _lib.pack_planes(canon, rows, cols, packed)
-                host = torch.empty(packed.numel(), dtype=torch.int32, pin_memory=True)
+                host = torch.empty(packed.numel(), dtype=torch.int32)
                 host.copy_(packed)
                 self.host_planes.append(host)
                 for b in range(3, 7):
-                    lut = torch.empty((rows, 1 << b), dtype=torch.int16, pin_memory=True)
+                    lut = torch.empty((rows, 1 << b), dtype=torch.int16)
                     lut.copy_(torch.from_numpy(np.ascontiguousarray(m.luts[b - 3]).view(np.int16)))
                     self.host_luts.append(lut)
                 w16 = None
@@ -64,7 +87,7 @@ class PagedExperts:
         self.pager = None
         self.layer = None
         self.bits = None
-        self.copy_stream = torch.cuda.Stream(device=device)
+        self.copy_stream = _copy_stream(device)
 
     def has_w16(self, e):
         return all(self.table.tensors[e][name]["w16"] is not None for name in MATS)
@@ -113,3 +136,6 @@ class PagedExperts:
         if self.pager is not None:
             self.pager.close()
             self.pager = None
+        if self.copy_stream is not None:
+            _hip().hipStreamDestroy(ctypes.c_void_p(self.copy_stream.cuda_stream))
+            self.copy_stream = None

@@ -13,6 +13,7 @@ device replicas so every step reads its planes from HBM rather than from the
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -156,13 +157,22 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     A second layer runs on paged weights (PagedExperts), its step captured as
     a HIP graph.  Each repetition demotes every bit-plane expert above 3 bits
     by one bit (committed, so only the lower LUTs move), enqueues `steps`
-    graph replays, stages the promotion back to `bits` (the plane and LUT
-    copies go out on the copy stream while those replays run; the host only
-    issues them), enqueues `steps` more replays and commits.  The host stays
-    far ahead of the GPU (a replay costs it microseconds, the GPU a whole
-    step), so the queue never drains: every step interval comes from GPU
-    events.  The steps whose interval overlaps the copy window, against the
-    mean of an idle run, give the loss."""
+    graph replays and, when two thirds of them are still queued, stages the
+    promotion back to `bits` (the host issues the copies; the copy engines
+    move them while the replays run), enqueues `steps` more replays, waits
+    for the copies and commits (the commit places the staged planes and LUTs
+    on the layer's stream; its time between two steps is `commit_us`).  The
+    host stays milliseconds ahead of the GPU, so every step interval comes
+    from GPU events.  The copy window opens at the event of the step the host
+    saw end just before staging and closes when the host sees a 4-byte
+    device-to-host copy, queued on the copy stream behind the staged copies,
+    land in pinned memory.  With the copy stream in the same hardware queue
+    as the layer's stream that copy waits for the replays queued before it,
+    so the window is an upper bound (`copy_ms_idle` times the same copies on
+    an idle GPU, with events on the copy stream).  The replays before the
+    window (same bitwidths, no copies) are the baseline; the steps that
+    overlap the window, against it, give the loss, and `lost_us` is the time
+    they took beyond the baseline, per re-plan."""
     import numpy as np
     import torch
     from any_precision_quantized_amd import _lib
@@ -179,9 +189,9 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     low = np.where((bits > 3) & (bits <= 6), bits - 1, bits).astype(np.int8)
     graph = lay.graph(x)
 
-    def event():
+    def event(s=stream):
         e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
+        e.record(s)
         return e
 
     def enqueue(n, evs):
@@ -189,55 +199,84 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
             graph.replay()
             evs.append(event())
 
-    def step_us(evs):
-        return [a.elapsed_time(b) * 1e3 for a, b in zip(evs[:-1], evs[1:])]
-
+    hip = ctypes.CDLL("libamdhip64.so")
+    flag_dev = [torch.full((1,), v, dtype=torch.int32, device="cuda") for v in (1, 2)]
+    flag_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    flag_view = flag_host.numpy()
     for _ in range(10):
         graph.replay()
     torch.cuda.synchronize()
-    evs = [event()]
-    enqueue(2 * steps, evs)
-    torch.cuda.synchronize()
-    idle = step_us(evs)
-    during, copy_ms, stage_us, h2d, d2d, ranges = [], [], [], 0, 0, 0
-    for _ in range(reps):
+    before, during, lost, copy_ms, stage_us, commit_us = [], [], [], [], [], []
+    for rep in range(reps):
         if pe.apply(low) != _lib.OK:
             raise RuntimeError("paging probe: demotion did not fit")
         torch.cuda.synchronize()
         evs = [event()]
         enqueue(steps, evs)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(pe.copy_stream)
-        t0 = time.perf_counter()
+        anchor = evs[-1 - max(5, 2 * steps // 3)]
+        give_up = time.perf_counter() + 30.0
+        while not anchor.query():
+            if time.perf_counter() > give_up:
+                raise RuntimeError("paging probe: the layer did not advance within 30 s")
+        ta = time.perf_counter()
         if pe.stage(bits) != _lib.OK:
             raise RuntimeError("paging probe: promotion did not fit")
-        stage_us.append((time.perf_counter() - t0) * 1e6)
-        c1.record(pe.copy_stream)
+        stage_us.append((time.perf_counter() - ta) * 1e6)
+        mark = rep % 2 + 1
+        if hip.hipMemcpyAsync(ctypes.c_void_p(flag_host.data_ptr()), ctypes.c_void_p(flag_dev[rep % 2].data_ptr()),
+                              ctypes.c_size_t(4), 2, ctypes.c_void_p(pe.copy_stream.cuda_stream)) != 0:
+            raise RuntimeError("paging probe: marker copy failed")
         enqueue(steps, evs)
+        while int(flag_view[0]) != mark:
+            if time.perf_counter() > give_up:
+                raise RuntimeError("paging probe: the copies did not finish within 30 s")
+        tb = time.perf_counter()
+        k0 = event()
+        pe.commit(bits)
+        k1 = event()
+        torch.cuda.synchronize()
+        commit_us.append(k0.elapsed_time(k1) * 1e3)
+        lo = evs[0].elapsed_time(anchor)
+        hi = lo + (tb - ta) * 1e3
+        copy_ms.append(hi - lo)
+        t = [evs[0].elapsed_time(e) for e in evs]
+        iv = [(t[i + 1] - t[i]) * 1e3 for i in range(len(t) - 1)]
+        base = [iv[i] for i in range(len(iv)) if t[i + 1] <= lo and i > 0]
+        over = [iv[i] for i in range(len(iv)) if t[i + 1] > lo and t[i] < hi]
+        before += base
+        during += over
+        lost.append(sum(over) - len(over) * float(np.mean(base)))
+    st = pe.stats()
+    # the same promotion on an idle GPU, timed on the copy stream
+    idle_ms = []
+    for _ in range(reps):
+        if pe.apply(low) != _lib.OK:
+            raise RuntimeError("paging probe: demotion did not fit")
+        torch.cuda.synchronize()
+        e0 = event(pe.copy_stream)
+        if pe.stage(bits) != _lib.OK:
+            raise RuntimeError("paging probe: promotion did not fit")
+        e1 = event(pe.copy_stream)
         pe.commit(bits)
         torch.cuda.synchronize()
-        st = pe.stats()
-        h2d, d2d, ranges = st["h2d"], st["d2d"], st["ranges"]
-        lo, hi = evs[0].elapsed_time(c0), evs[0].elapsed_time(c1)
-        copy_ms.append(hi - lo)
-        for i, us in enumerate(step_us(evs)):
-            a, b = evs[0].elapsed_time(evs[i]), evs[0].elapsed_time(evs[i + 1])
-            if b > lo and a < hi:
-                during.append(us)
+        idle_ms.append(e0.elapsed_time(e1))
     del graph
     pe.close()
-    idle_us = float(np.mean(idle))
-    during_us = float(np.mean(during)) if during else None
-    cm = float(np.mean(copy_ms))
+    base_us, dur_us = float(np.mean(before)), float(np.mean(during))
+    cm, ci = float(np.mean(copy_ms)), float(np.median(idle_ms))
+    h2d = int(st["h2d"])
     return {"replan": "every bit-plane expert above 3 bits promoted by one plane (b-1 -> b) while the layer runs",
-            "copy_ranges": int(ranges),
+            "copy_ranges": int(st["ranges"]),
             "stage_host_us": round(float(np.median(stage_us)), 1),
-            "h2d_bytes": int(h2d), "d2d_bytes": int(d2d), "copy_ms": round(cm, 3),
-            "h2d_GBps": round(h2d / (cm * 1e-3) / 1e9, 2) if cm > 0 else None,
-            "step_us_idle": round(idle_us, 2),
-            "step_us_during_copy": None if during_us is None else round(during_us, 2),
+            "commit_us": round(float(np.median(commit_us)), 1),
+            "h2d_bytes": h2d, "d2d_bytes": int(st["d2d"]),
+            "copy_ms_idle": round(ci, 3), "h2d_GBps": round(h2d / (ci * 1e-3) / 1e9, 2),
+            "copy_ms": round(cm, 3),
+            "step_us_before": round(base_us, 2),
+            "step_us_during_copy": round(dur_us, 2),
             "steps_overlapping_copy": len(during),
-            "loss": None if during_us is None else round(during_us / idle_us - 1.0, 4)}
+            "loss": round(dur_us / base_us - 1.0, 4),
+            "lost_us": round(float(np.mean(lost)), 1)}
 
 
 def codec_probe(inp, reps=5):

@@ -370,40 +370,58 @@ int apmoe_arena_stats(const apmoe_arena* arena, uint64_t* free_bytes, uint64_t* 
  *  create  host_planes [3E]: per expert gate, up, down, the six packed slabs
  *          (apmoe_packed_plane_words(rows, cols) words, as apmoe_pack_planes
  *          writes them); host_luts [3E][4]: fp16 [rows][1 << b] for b = 3..6.
- *          Host memory that must outlive the pager and stay unchanged; it
- *          should be pinned (hipHostMalloc) so the copies run asynchronously.
+ *          Read only during create: the pager keeps its own pinned copy
+ *          (hipHostMalloc), laid out by expert and promotion step so that
+ *          raising an expert by one bit is one contiguous range.
  *          arena: device memory (256-byte aligned, arena_bytes) owned by the
- *          caller; the pager keeps a patch buffer in it.  experts: the device
+ *          caller; the pager keeps a patch buffer and a copy list (28 bytes
+ *          x 18E) in it.  experts: the device
  *          descriptors of these E experts (gate/up/down planes and lut words
  *          are written by commits; w16 words are left alone); bits: their
  *          device bits table.  Nothing is resident until the first commit.
- *          APMOE_ENOSPACE if the arena cannot hold the patch buffer.
+ *          APMOE_ENOSPACE if the arena cannot hold the patch buffer and copy
+ *          list.
  *  stage   bits_new [E] (host): enqueue on copy_stream the copies that make
- *          the new residency (host-to-device copies of the planes and LUTs
- *          that become resident; a block that cannot grow in place is moved,
- *          its resident planes copied device to device) and record what the
- *          commit retires.  Each range is one hipMemcpyAsync (the copy
- *          engines move it; no compute unit takes part).  The layer keeps running at the old bitwidths
- *          meanwhile.  APMOE_EBITS for a bitwidth outside {3,4,5,6,16};
+ *          the new residency and record what the commit retires.  The new
+ *          planes and LUTs go host to device (one hipMemcpyAsync per expert
+ *          and bitwidth step, on the copy engines) into a staging block of
+ *          the arena, which the commit places; a block that cannot grow in
+ *          place is moved, its resident planes copied device to device by the
+ *          commit.  When the arena has no room for the staging block, each
+ *          matrix's planes of one step and each LUT are copied host to device
+ *          straight into place.  The staging block returns to the arena with
+ *          the blocks the commit retires.  copy_stream gets copies only, no
+ *          kernel or event (an event queued behind the copies would hold up,
+ *          until they finish, every stream sharing its hardware queue); it
+ *          must stay valid until the commit (or destroy).  The layer keeps
+ *          running at the old bitwidths meanwhile.
+ *          APMOE_EBITS for a bitwidth outside {3,4,5,6,16};
  *          APMOE_ENOSPACE (nothing staged, nothing enqueued) when the arena
  *          cannot hold the new blocks even after waiting for retired blocks;
- *          APMOE_EINVAL if a staged change is not yet committed.  Waits on the
- *          host for the previous commit to have executed.
- *  commit  on stream: wait for the staged copies, then write the plane and
- *          LUT pointers of every paged matrix and the bits table together
- *          (one kernel), so every later kernel on stream sees the new
- *          bitwidths and every earlier one the old.  Blocks the change retires
- *          return to the arena once the stream has passed the commit.  All
- *          kernels that read these experts must be ordered on stream.
+ *          APMOE_EINVAL if a staged change is not yet committed (or, with
+ *          nothing enqueued, if a planned copy fell outside the arena or the
+ *          host copy).  Waits on the host for the previous commit to have
+ *          executed.
+ *  commit  on stream: record an event on the stage's copy_stream and wait for
+ *          it (the staged copies), place the staged planes and LUTs and move
+ *          the relocated blocks (one kernel, when there is anything to place),
+ *          then write the plane and LUT pointers of every paged matrix and the
+ *          bits table together (one kernel), so every later kernel on stream
+ *          sees the new bitwidths and every earlier one the old.  Blocks the
+ *          change retires return to the arena once the stream has passed the
+ *          commit.  All kernels that read these experts must be ordered on
+ *          stream.
  *  stats   resident plane and LUT bytes, arena free bytes and largest free
- *          range, the bytes the last stage copied host to device and device
- *          to device, and the number of ranges it copied (any pointer may be
+ *          range, the plane and LUT bytes the last stage copied host to
+ *          device, the resident plane bytes it moved to new blocks, and the
+ *          number of host-to-device ranges it copied (any pointer may be
  *          NULL).
  *  destroy waits for outstanding copies and commits; the arena stays the
  *          caller's.
  * Host resources and waits (the pager is the library's one stateful object):
- * create allocates the pager, a pinned host patch buffer (hipHostMalloc) and
- * two HIP events, all freed by destroy; a commit that retires blocks creates
+ * create allocates the pager, its pinned host copy of the planes and LUTs,
+ * a pinned patch buffer and copy list (hipHostMalloc) and two HIP events, all
+ * freed by destroy; a commit that retires blocks creates
  * one more event, destroyed once those blocks are back in the arena.  stage
  * waits on the host (hipEventSynchronize) for the previous commit to have run,
  * and, when the arena is short, for the retired blocks; if enqueueing a copy

@@ -1,7 +1,7 @@
 // Host-side fuzz driver for the library's plain C++ parts, built with the
 // address and undefined-behaviour sanitizers by tests/test_host_sanitize.py:
 // the first-fit arena (C ABI), the plane-paging residency bookkeeping
-// (claims, rollback, retirement), the greedy and online planners with their
+// (claims, rollback, retirement) and the pager's copy plans, the greedy and online planners with their
 // routing multipliers, and the exponent encoder (round trip through a CPU
 // decode of the stream it writes).  Exits non-zero on a failed check; the
 // sanitizers abort on a memory or undefined-behaviour error.
@@ -142,6 +142,141 @@ static int residency_fuzz(Rng& rng) {
     return 0;
 }
 
+// Copy plans of the pager, staged and direct, run on a byte model of the
+// arena: the device-side copies of one stage (one kernel, all concurrent)
+// neither overlap one another's destinations nor read what another writes,
+// the host-to-device bytes are exactly the new planes and LUTs, and after
+// every commit each resident block holds the host copy's planes and LUT.
+static bool overlap(uint64_t a, uint64_t an, uint64_t b, uint64_t bn) { return a < b + bn && b < a + an; }
+
+static int copy_plan_fuzz(Rng& rng) {
+    using namespace apmoe;
+    uint64_t n_staged = 0, n_direct = 0, n_moves = 0, n_multi = 0, n_demote = 0, n_merged = 0;
+    for (int trial = 0; trial < 40; ++trial) {
+        const int E = (int)uni(rng, 1, 8);
+        std::vector<MatResidency> mats(3 * E);
+        for (auto& m : mats) {
+            m.slab = 256 * uni(rng, 1, 4);
+            const uint64_t l = 256 * uni(rng, 1, 3);
+            for (int b = 3; b <= 6; ++b) m.lut_bytes[b - 3] = l << (b - 3);
+        }
+        const HostLayout L = host_layout(mats);
+        std::vector<uint8_t> host(L.bytes);
+        for (auto& c : host) c = (uint8_t)uni(rng, 0, 255);
+        // every plane and LUT sits at its own bytes of the host copy
+        std::vector<uint8_t> seen(L.bytes, 0);
+        for (int e = 0; e < E; ++e)
+            for (int j = 0; j < 3; ++j) {
+                const MatResidency& m = mats[3 * e + j];
+                for (int p = 0; p < 6; ++p) {
+                    const uint64_t o = host_plane_off(mats, L, e, j, p);
+                    CHECK(o + m.slab <= L.bytes);
+                    for (uint64_t i = o; i < o + m.slab; ++i) CHECK(seen[i]++ == 0);
+                }
+                for (int b = 3; b <= 6; ++b) {
+                    const uint64_t o = host_lut_off(mats, L, e, j, b);
+                    CHECK(o + m.lut_bytes[b - 3] <= L.bytes);
+                    for (uint64_t i = o; i < o + m.lut_bytes[b - 3]; ++i) CHECK(seen[i]++ == 0);
+                }
+            }
+        for (uint8_t c : seen) CHECK(c == 1);
+        const uint64_t size = 256 * uni(rng, 100, 1500);
+        apmoe_arena arena;
+        arena.size = size;
+        arena.free_[0] = size;
+        std::vector<uint8_t> mem(size, 0);
+        std::vector<Block> pending;
+        for (int step = 0; step < 40; ++step) {
+            for (const Block& b : pending) CHECK(arena.release(b.off, b.len));
+            pending.clear();
+            const int levels[5] = {0, 3, 4, 5, 6};
+            for (int e = 0; e < E; ++e) {
+                const int w = levels[uni(rng, 0, 4)];
+                for (int j = 0; j < 3; ++j) mats[3 * e + j].want = w;
+            }
+            if (!claim(arena, mats)) {
+                unstage(arena, mats);
+                continue;
+            }
+            CopyPlan plan = plan_copies(mats, L, true, 0);
+            CHECK(plan.ok);
+            Block staging;
+            uint64_t soff = 0;
+            const bool staged = uni(rng, 0, 3) != 0 && plan.staged_bytes && arena.alloc(plan.staged_bytes, &soff);
+            const uint64_t cap = uni(rng, 0, 1) ? 256 * uni(rng, 1, 8) : 0;
+            if (staged) {
+                staging = Block{soff, align_up(plan.staged_bytes)};
+                plan = plan_copies(mats, L, true, soff, cap);
+            } else {
+                plan = plan_copies(mats, L, false, 0, cap);
+            }
+            for (const Copy& c : plan.h2d) CHECK(c.bytes > 0 && (!cap || c.bytes <= cap));
+            CHECK(plan.ok && plan.dev.size() <= (size_t)18 * E);
+            ++(staged ? n_staged : n_direct);
+            for (const MatResidency& m : mats) {
+                n_moves += m.moved && m.have;
+                n_multi += m.want > m.have + 1;
+                n_demote += m.want && m.want < m.have;
+            }
+            uint64_t want_h2d = 0, got_h2d = 0;
+            for (const MatResidency& m : mats) {
+                if (m.want > m.have) want_h2d += (uint64_t)(m.want - m.have) * m.slab;
+                if (m.new_lut) want_h2d += m.lut_bytes[m.want - 3];
+            }
+            for (const Copy& c : plan.h2d) {
+                CHECK(c.src + c.bytes <= L.bytes && c.dst + c.bytes <= size);
+                if (staged) CHECK(c.dst >= staging.off && c.dst + c.bytes <= staging.off + staging.len);
+                got_h2d += c.bytes;
+                std::copy(host.begin() + c.src, host.begin() + c.src + c.bytes, mem.begin() + c.dst);
+            }
+            CHECK(got_h2d == want_h2d);
+            if (staged && !cap) {   // one range per run of adjacent step blocks: fewer than the blocks when any merged
+                size_t blocks = 0;
+                for (int e = 0; e < E; ++e) {
+                    const MatResidency& m = mats[3 * e];
+                    blocks += m.want > m.have ? m.want - std::max(m.have, 2) : m.new_lut;
+                }
+                CHECK(plan.h2d.size() <= blocks);
+                n_merged += blocks - plan.h2d.size();
+            }
+            for (size_t a = 0; a < plan.dev.size(); ++a) {
+                const Copy& x = plan.dev[a];
+                CHECK(x.src % 16 == 0 && x.dst % 16 == 0 && x.bytes % 16 == 0);
+                CHECK(x.src + x.bytes <= size && x.dst + x.bytes <= size);
+                for (size_t b = 0; b < plan.dev.size(); ++b) {
+                    const Copy& y = plan.dev[b];
+                    CHECK(!overlap(x.dst, x.bytes, y.src, y.bytes));
+                    if (a != b) CHECK(!overlap(x.dst, x.bytes, y.dst, y.bytes));
+                }
+            }
+            const std::vector<uint8_t> snap = mem;   // the kernel's copies all read the state before it
+            for (const Copy& c : plan.dev)
+                std::copy(snap.begin() + c.src, snap.begin() + c.src + c.bytes, mem.begin() + c.dst);
+            pending = retired_blocks(mats);
+            if (staging.len) pending.push_back(staging);
+            adopt(mats);
+            for (int e = 0; e < E; ++e)
+                for (int j = 0; j < 3; ++j) {
+                    const MatResidency& m = mats[3 * e + j];
+                    CHECK(m.planes.len == (uint64_t)m.have * m.slab);
+                    for (int p = 0; p < m.have; ++p)
+                        CHECK(std::equal(mem.begin() + m.planes.off + p * m.slab,
+                                         mem.begin() + m.planes.off + (p + 1) * m.slab,
+                                         host.begin() + host_plane_off(mats, L, e, j, p)));
+                    if (m.have)
+                        CHECK(std::equal(mem.begin() + m.lut.off, mem.begin() + m.lut.off + m.lut_bytes[m.have - 3],
+                                         host.begin() + host_lut_off(mats, L, e, j, m.have)));
+                }
+        }
+    }
+    printf("copy plans: %llu staged (%llu step blocks merged into a neighbour's range), %llu direct; matrices moved "
+           "%llu, raised by several steps %llu, demoted %llu\n",
+           (unsigned long long)n_staged, (unsigned long long)n_merged, (unsigned long long)n_direct,
+           (unsigned long long)n_moves, (unsigned long long)n_multi, (unsigned long long)n_demote);
+    CHECK(n_staged && n_merged && n_direct && n_moves && n_multi && n_demote);
+    return 0;
+}
+
 static int planner_fuzz(Rng& rng) {
     const int8_t all_levels[5] = {16, 6, 5, 4, 3};
     for (int trial = 0; trial < 200; ++trial) {
@@ -256,8 +391,9 @@ int main() {
     Rng rng(20261203);
     if (arena_fuzz(rng)) return 1;
     if (residency_fuzz(rng)) return 1;
+    if (copy_plan_fuzz(rng)) return 1;
     if (planner_fuzz(rng)) return 1;
     if (codec_fuzz(rng)) return 1;
-    printf("host sanitize: arena, residency, planners, exponent codec clean\n");
+    printf("host sanitize: arena, residency, copy plans, planners, exponent codec clean\n");
     return 0;
 }

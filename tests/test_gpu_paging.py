@@ -104,6 +104,8 @@ def test_paged_layer_follows_every_plan(cfg):
                 assert st["h2d"] == paging.host_to_device_bytes(cfg.H, cfg.I, prev, bits)
         if bits is PLANS[0]:
             assert st["d2d"] > 0, "blocks packed back to back: a promotion moves them"
+            # staged: one host-to-device range per expert and step
+            assert st["ranges"] <= sum(max(0, 6 - (0 if b == 16 else b)) for b in prev), st
         _check_resident(pe, layer, bits)
         got = _forward(inp, layer)
         G.check_out({"out": got}, moe.layer(inp, bits=np.asarray(bits, np.int8)))
@@ -158,6 +160,30 @@ def test_paging_enospace_keeps_the_plan():
     assert pe.apply([6] * cfg.E) == _lib.ENOSPACE
     after = pe.stats()
     assert after["resident"] == before["resident"] and after["free"] == before["free"]
+    _check_resident(pe, layer, [3] * cfg.E)
+    G.check_out({"out": _forward(inp, layer)}, moe.layer(inp, bits=np.full(cfg.E, 3, np.int8)))
+    pe.close()
+
+
+def test_paging_copies_into_place_without_room_to_stage():
+    """An arena that holds the 3-bit blocks and the moved 6-bit blocks side by
+    side but not a staging block as well: the promotion copies each matrix's
+    planes and LUT straight into place (three plane ranges per step and three
+    LUT ranges per expert), and the result is the same."""
+    cfg = PAGED
+    routed = [e for e in range(cfg.E)]
+    arena = paging.resident_bytes(cfg.H, cfg.I, [3] * cfg.E) + paging.resident_bytes(cfg.H, cfg.I, [6] * cfg.E) \
+        + 64 * 1024
+    inp, pe, layer = _paged(cfg, [3] * cfg.E, arena_bytes=arena)
+    assert pe.apply([6] * cfg.E) == _lib.OK
+    st = pe.stats()
+    assert st["ranges"] == len(routed) * (3 * 3 + 3), st
+    assert st["h2d"] == paging.host_to_device_bytes(cfg.H, cfg.I, [3] * cfg.E, [6] * cfg.E)
+    assert st["d2d"] > 0
+    _check_resident(pe, layer, [6] * cfg.E)
+    G.check_out({"out": _forward(inp, layer)}, moe.layer(inp, bits=np.full(cfg.E, 6, np.int8)))
+    # and back down: the 3-bit LUTs only, staged now that the old 3-bit blocks are free again
+    assert pe.apply([3] * cfg.E) == _lib.OK
     _check_resident(pe, layer, [3] * cfg.E)
     G.check_out({"out": _forward(inp, layer)}, moe.layer(inp, bits=np.full(cfg.E, 3, np.int8)))
     pe.close()
