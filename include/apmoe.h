@@ -419,14 +419,16 @@ int apmoe_arena_stats(const apmoe_arena* arena, uint64_t* free_bytes, uint64_t* 
  *  destroy waits for outstanding copies and commits; the arena stays the
  *          caller's.
  * Host resources and waits (the pager is the library's one stateful object):
- * create allocates the pager, its pinned host copy of the planes and LUTs,
- * a pinned patch buffer and copy list (hipHostMalloc) and two HIP events, all
- * freed by destroy; a commit that retires blocks creates
- * one more event, destroyed once those blocks are back in the arena.  stage
- * waits on the host (hipEventSynchronize) for the previous commit to have run,
- * and, when the arena is short, for the retired blocks; if enqueueing a copy
- * fails it synchronises copy_stream before undoing the claims.  destroy waits
- * for every outstanding copy and commit.
+ * create allocates the pager, its pinned host copy of the planes and LUTs
+ * (as many bytes as all planes and LUTs of the E experts), a pinned patch
+ * buffer and copy list (hipHostMalloc) and two HIP events, all freed by
+ * destroy; a commit that retires blocks creates one more event, destroyed
+ * once those blocks are back in the arena.  stage waits on the host
+ * (hipEventSynchronize) for the previous commit to have run, and, when the
+ * arena is short, for the retired blocks; if enqueueing a copy fails it
+ * synchronises copy_stream before undoing the claims.  destroy synchronises
+ * the copy_stream of a stage not yet committed and waits for the last
+ * commit.
  * Needs 1 <= E <= APMOE_MAX_EXPERTS, H % 32 == 0, I % 32 == 0.
  */
 typedef struct apmoe_pager apmoe_pager;
