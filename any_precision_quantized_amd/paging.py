@@ -25,20 +25,58 @@ def _hip():
     return ctypes.CDLL("libamdhip64.so")
 
 
-def _copy_stream(device):
-    """A non-blocking stream made with HIP itself for the pager's copies.
-    HIP spreads streams over a few hardware queues and gives a new one the
-    least used; torch's pool streams are handed out round-robin, so one of
-    them lands in the queue of the default stream one time in four.  A copy
-    stream that shares the layer stream's queue was measured to slow the
-    layer's steps about twofold while the copies run."""
+def _shares_queue(busy, cand):
+    """True when `cand` sits in the same hardware queue as `busy`: an event
+    recorded on the idle `cand` behind a few milliseconds of spinning on
+    `busy` is still pending half a millisecond later, while the spin is.  In
+    a queue of its own it completes at once."""
+    import time
+
     import torch
-    with torch.cuda.device(device):
-        s = ctypes.c_void_p()
-        rc = _hip().hipStreamCreateWithFlags(ctypes.byref(s), ctypes.c_uint(1))   # hipStreamNonBlocking
-        if rc != 0:
-            raise RuntimeError(f"hipStreamCreateWithFlags failed ({rc})")
-        return torch.cuda.ExternalStream(s.value, device=device)
+    with torch.cuda.stream(busy):
+        torch.cuda._sleep(10_000_000)   # a few ms of one spinning wave
+        spun = torch.cuda.Event()
+        spun.record(busy)
+    mark = torch.cuda.Event()
+    mark.record(cand)
+    time.sleep(0.0005)
+    waited = not mark.query() and not spun.query()
+    busy.synchronize()
+    cand.synchronize()
+    return waited
+
+
+def _copy_stream(device):
+    """A non-blocking stream made with HIP itself for the pager's copies, in a
+    hardware queue other than the current stream's.  Streams share a few
+    hardware queues (four per process here).  A copy stream in the layer
+    stream's queue was measured to make the copies' completion visible only
+    once the layer's queued work had run, and an event recorded on it behind
+    the copies to hold the layer up for the whole copy, so candidates that
+    share the current stream's queue are set aside (and destroyed)."""
+    import torch
+    hip = _hip()
+    busy = torch.cuda.current_stream(device)
+    rejected = []
+    chosen = None
+    try:
+        with torch.cuda.device(device):
+            for _ in range(8):
+                s = ctypes.c_void_p()
+                rc = hip.hipStreamCreateWithFlags(ctypes.byref(s), ctypes.c_uint(1))   # hipStreamNonBlocking
+                if rc != 0:
+                    raise RuntimeError(f"hipStreamCreateWithFlags failed ({rc})")
+                cand = torch.cuda.ExternalStream(s.value, device=device)
+                if not _shares_queue(busy, cand):
+                    chosen = cand
+                    break
+                rejected.append(s.value)
+            if chosen is None:   # every candidate shared it: keep the last
+                chosen = torch.cuda.ExternalStream(rejected.pop(), device=device)
+    finally:
+        for v in rejected:
+            hip.hipStreamDestroy(ctypes.c_void_p(v))
+    return chosen
 
 
 def arena_bytes_for(H, I, E, bits_max=6, slack=1.25):

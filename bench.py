@@ -168,11 +168,13 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     device-to-host copy, queued on the copy stream behind the staged copies,
     land in pinned memory.  With the copy stream in the same hardware queue
     as the layer's stream that copy waits for the replays queued before it,
-    so the window is an upper bound (`copy_ms_idle` times the same copies on
-    an idle GPU, with events on the copy stream).  The replays before the
+    so the window would be an upper bound; PagedExperts picks a copy stream
+    outside the current stream's queue (`copy_ms_idle` times the same copies
+    on an idle GPU, with events on the copy stream).  The replays before the
     window (same bitwidths, no copies) are the baseline; the steps that
     overlap the window, against it, give the loss, and `lost_us` is the time
-    they took beyond the baseline, per re-plan."""
+    every replay after the stage call took beyond the baseline, per re-plan
+    (wherever the copies landed)."""
     import numpy as np
     import torch
     from any_precision_quantized_amd import _lib
@@ -243,9 +245,10 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
         iv = [(t[i + 1] - t[i]) * 1e3 for i in range(len(t) - 1)]
         base = [iv[i] for i in range(len(iv)) if t[i + 1] <= lo and i > 0]
         over = [iv[i] for i in range(len(iv)) if t[i + 1] > lo and t[i] < hi]
+        after = [iv[i] for i in range(len(iv)) if t[i + 1] > lo]
         before += base
         during += over
-        lost.append(sum(over) - len(over) * float(np.mean(base)))
+        lost.append(sum(after) - len(after) * float(np.mean(base)))
     st = pe.stats()
     # the same promotion on an idle GPU, timed on the copy stream
     idle_ms = []
