@@ -151,11 +151,14 @@ def counted_traffic(kernel, workload):
     return None
 
 
-def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
+def paging_probe(cfg, inp, bits, mfma_min, R=1, steps=60, reps=3):
     """Throughput while a re-plan's plane copies run (plane paging).
 
-    A second layer runs on paged weights (PagedExperts), its step captured as
-    a HIP graph.  Each repetition demotes every bit-plane expert above 3 bits
+    R copies of the layer run on paged weights (PagedExperts, one arena and
+    pager each), their steps captured as HIP graphs and replayed in turn, so
+    that, as in the timed steps, each step reads its weights from HBM rather
+    than from the memory-side cache; the first copy is re-planned.  Each
+    repetition demotes every bit-plane expert above 3 bits
     by one bit (committed, so only the lower LUTs move), enqueues `steps`
     graph replays and, when two thirds of them are still queued, stages the
     promotion back to `bits` (the host issues the copies; the copy engines
@@ -181,15 +184,20 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
     from any_precision_quantized_amd import layer as L
     from any_precision_quantized_amd.paging import PagedExperts, arena_bytes_for
 
-    pe = PagedExperts(inp.experts, cfg.H, cfg.I, arena_bytes_for(cfg.H, cfg.I, cfg.E))
-    shared = L.ExpertTable([inp.shared]) if inp.shared is not None else None
-    lay = L.MoELayer(cfg.E, cfg.H, cfg.I, cfg.k, cfg.T, inp.w_router, inp.bias, cfg.logit_scale, pe.table, bits,
-                     shared, cfg.shared_I, mfma_min)
-    pe.attach(lay, bits)
     x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).cuda().view(torch.float16)
+    pes, graphs = [], []
+    for _ in range(max(1, R)):
+        p_ = PagedExperts(inp.experts, cfg.H, cfg.I, arena_bytes_for(cfg.H, cfg.I, cfg.E))
+        shared = L.ExpertTable([inp.shared]) if inp.shared is not None else None
+        lay = L.MoELayer(cfg.E, cfg.H, cfg.I, cfg.k, cfg.T, inp.w_router, inp.bias, cfg.logit_scale, p_.table, bits,
+                         shared, cfg.shared_I, mfma_min)
+        p_.attach(lay, bits)
+        pes.append(p_)
+        graphs.append(lay.graph(x))
+    pe = pes[0]
     stream = torch.cuda.current_stream()
     low = np.where((bits > 3) & (bits <= 6), bits - 1, bits).astype(np.int8)
-    graph = lay.graph(x)
+    turn = [0]
 
     def event(s=stream):
         e = torch.cuda.Event(enable_timing=True)
@@ -198,15 +206,16 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
 
     def enqueue(n, evs):
         for _ in range(n):
-            graph.replay()
+            graphs[turn[0] % len(graphs)].replay()
+            turn[0] += 1
             evs.append(event())
 
     hip = ctypes.CDLL("libamdhip64.so")
     flag_dev = [torch.full((1,), v, dtype=torch.int32, device="cuda") for v in (1, 2)]
     flag_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
     flag_view = flag_host.numpy()
-    for _ in range(10):
-        graph.replay()
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
     before, during, lost, copy_ms, stage_us, commit_us = [], [], [], [], [], []
     for rep in range(reps):
@@ -263,8 +272,9 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
         pe.commit(bits)
         torch.cuda.synchronize()
         idle_ms.append(e0.elapsed_time(e1))
-    del graph
-    pe.close()
+    del graphs
+    for p_ in pes:
+        p_.close()
     base_us, dur_us = float(np.mean(before)), float(np.mean(during))
     cm, ci = float(np.mean(copy_ms)), float(np.median(idle_ms))
     h2d = int(st["h2d"])
@@ -279,6 +289,7 @@ def paging_probe(cfg, inp, bits, mfma_min, steps=60, reps=3):
             "step_us_during_copy": round(dur_us, 2),
             "steps_overlapping_copy": len(during),
             "loss": round(dur_us / base_us - 1.0, 4),
+            "paged_layers": len(pes),
             "lost_us": round(float(np.mean(lost)), 1)}
 
 
@@ -717,7 +728,7 @@ def main():
     if not args.no_workloads:
         result["workloads"] = other_workloads(args, cfg.name)
     if not args.no_paging_probe:
-        result["paging"] = paging_probe(cfg, inp, bits, mfma_min)
+        result["paging"] = paging_probe(cfg, inp, bits, mfma_min, R=result["config"]["weight_replicas"])
     if not args.no_codec_probe:
         result["exp_codec"] = codec_probe(inp, reps=10)
     result["planner"] = planner_probe(inp)
