@@ -14,8 +14,9 @@
 // pinned host copy over the bus was measured, and its long-latency reads
 // slowed the layer running beside it by about 40%.  Each copy costs about
 // 9 us beyond its bytes, so the pager keeps its own pinned host copy laid out
-// by expert and promotion step (residency.hpp): raising an expert by one
-// step is one range, copied into a staging block of the arena.  The commit
+// by promotion step and then expert (residency.hpp): raising an expert by one
+// step is one range, and so is raising experts with adjacent indices to the
+// same step; the ranges are copied into a staging block of the arena.  The commit
 // then places every staged plane and LUT (and moves the relocated blocks)
 // with one short kernel on the compute stream, ahead of the pointer patch.
 // The copy stream carries copies only, and stage records no event on it:
@@ -103,8 +104,9 @@ __global__ __launch_bounds__(256) void pager_place_kernel(char* __restrict__ bas
 
 constexpr int kPlaceBlocks = 2048;
 
-// Largest host-to-device copy (0: none).  Limits of 1 to 16 MB were
-// measured to change nothing but the number of copies.
+// Largest host-to-device copy (0: none).  Limits of 256 KB to 16 MB were
+// measured: they slow the copies (to 19 GB/s at 256 KB) without lowering what
+// the layer loses per step while copies run, so the total loss grows.
 constexpr uint64_t kMaxCopy = 0;
 
 // One patch list and the staged bits, laid out as the commit kernel reads them.
@@ -144,7 +146,7 @@ struct apmoe_pager {
     uint64_t dev_buf = 0;            // its device copy, carved from the arena
     size_t buf_bytes = 0;
     HostLayout layout;               // of host_copy
-    char* host_copy = nullptr;       // pinned planes and LUTs by expert and step
+    char* host_copy = nullptr;       // pinned planes and LUTs by promotion step, then expert
     char* place_host = nullptr;      // pinned staging of the device-side copy list and its chunk starts
     uint64_t place_dev = 0;          // its device copy, carved from the arena
     size_t max_place = 0;            // entries it holds
@@ -243,7 +245,7 @@ extern "C" int apmoe_pager_create(int E, int H, int I, const void* const* host_p
                            hipEventCreateWithFlags(&pg->last_commit, hipEventDisableTiming) != hipSuccess))
         rc = APMOE_EHIP;
     if (rc == APMOE_OK) {
-        // the caller's planes and LUTs, rearranged by expert and step
+        // the caller's planes and LUTs, rearranged by step and expert
         for (int e = 0; e < E; ++e)
             for (int j = 0; j < 3; ++j) {
                 const PagedMat& m = pg->mats[3 * e + j];

@@ -371,8 +371,9 @@ int apmoe_arena_stats(const apmoe_arena* arena, uint64_t* free_bytes, uint64_t* 
  *          (apmoe_packed_plane_words(rows, cols) words, as apmoe_pack_planes
  *          writes them); host_luts [3E][4]: fp16 [rows][1 << b] for b = 3..6.
  *          Read only during create: the pager keeps its own pinned copy
- *          (hipHostMalloc), laid out by expert and promotion step so that
- *          raising an expert by one bit is one contiguous range.
+ *          (hipHostMalloc), laid out by promotion step and then expert, so
+ *          that raising an expert by one bit is one contiguous range (and
+ *          raising experts with adjacent indices to the same bitwidth too).
  *          arena: device memory (256-byte aligned, arena_bytes) owned by the
  *          caller; the pager keeps a patch buffer and a copy list (28 bytes
  *          x 18E) in it.  experts: the device
