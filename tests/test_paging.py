@@ -169,6 +169,26 @@ def test_pager_create_argument_errors():
     assert lib.apmoe_pager_destroy(None) == _lib.OK
 
 
+def test_pager_binding_rejects_short_host_copies():
+    """The pager reads the host planes and LUTs once, at create: the binding
+    refuses host tensors smaller than a matrix's packed planes or b-bit LUT
+    before any library call."""
+    import torch
+    E, H, I = 2, 64, 96
+    planes = [torch.zeros(_lib.packed_plane_words(I if i % 3 < 2 else H, H if i % 3 < 2 else I), dtype=torch.int32)
+              for i in range(3 * E)]
+    luts = [torch.zeros((I if (i // 4) % 3 < 2 else H, 1 << (3 + i % 4)), dtype=torch.int16) for i in range(12 * E)]
+    dummy = torch.zeros(1)
+    short = list(planes)
+    short[4] = planes[4][:-1]   # expert 1, up: one word short
+    with pytest.raises(ValueError, match="host planes 4"):
+        _lib.Pager(E, H, I, short, luts, dummy, dummy, dummy)
+    short = list(luts)
+    short[4 * 5 + 2] = luts[4 * 5 + 2][:-1]   # expert 1, down, 5-bit LUT: one row short
+    with pytest.raises(ValueError, match="host LUT 5, 5 bits"):
+        _lib.Pager(E, H, I, planes, short, dummy, dummy, dummy)
+
+
 class _FakePager:
     """Stands in for PagedExperts on the host: records the plans it is asked
     to make resident and answers with a fixed status."""
