@@ -189,6 +189,46 @@ def test_paging_copies_into_place_without_room_to_stage():
     pe.close()
 
 
+@pytest.mark.parametrize("seed,room", [(1, "roomy"), (2, "middle"), (3, "tight")])
+def test_paging_random_plans(seed, room):
+    """Seeded random plans on the ragged layer in three arena sizes (twice the
+    6-bit residency; the 3-bit and the 6-bit residency side by side; the 6-bit
+    residency alone, plus 256 KB): stages go through the staging block,
+    straight into place when it does not fit, or fail with ENOSPACE and change
+    nothing.  After every plan the resident blocks equal the host copy and the
+    layer equals the oracle at the bitwidths in force."""
+    cfg = RAGGED
+    rng = np.random.default_rng(seed)
+    lo = paging.resident_bytes(cfg.H, cfg.I, [3] * cfg.E)
+    hi = paging.resident_bytes(cfg.H, cfg.I, [6] * cfg.E)
+    arena = {"roomy": 2 * hi, "middle": lo + hi, "tight": hi}[room] + 256 * 1024
+    bits = [int(b) for b in cfg.bits]
+    inp, pe, layer = _paged(cfg, bits, arena_bytes=arena)
+    G.say(f"paging random plans seed {seed}")
+    staged = direct = refused = 0
+    for _ in range(10):
+        new = [int(rng.choice([3, 4, 5, 6])) for _ in range(cfg.E)]
+        if rng.random() < 0.5:
+            new[4] = 16                               # the expert with fp16 weights
+        rc = pe.apply(new)
+        if rc == _lib.ENOSPACE:
+            refused += 1
+        else:
+            assert rc == _lib.OK
+            st = pe.stats()
+            moved = sum(max(0, (0 if b == 16 else b) - (0 if a == 16 else a)) for a, b in zip(bits, new))
+            if moved:   # a promotion: staged ranges are at most one per expert and step
+                staged += st["ranges"] <= moved
+                direct += st["ranges"] > moved
+            bits = new
+        _check_resident(pe, layer, bits)
+        G.check_out({"out": _forward(inp, layer)}, moe.layer(inp, bits=np.asarray(bits, np.int8)))
+    G.say(f"  {room}: staged {staged} direct {direct} refused {refused}")
+    # each arena reaches the path it is sized for (the plans are seeded)
+    assert {"roomy": staged, "middle": direct, "tight": refused}[room] > 0
+    pe.close()
+
+
 def test_paged_qwen_decode_full_size():
     """The Qwen-shaped decode layer (60 experts, four always-on fp16 experts
     in front of them in the descriptor table) on paged weights, before and
