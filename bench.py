@@ -562,6 +562,44 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
         del graphs
     ms_per_step = dt / steps * 1e3
     tokens_per_s = T * steps / dt
+
+    # The heavy launches' average durations from HIP graphs of that launch
+    # alone: 4R launches over the weight replicas in turn, replayed with events
+    # on the stream around the replays.  This is the kernels' own time; an
+    # event pair around one eager launch also holds its dispatch gap.
+    def launch_graph_us(name, reps=4):
+        nonlocal sp
+        fns = [next(fn for n_, fn, _ in seqs[r] if n_ == name) for r in range(R)]
+        n = 4 * R
+        g = torch.cuda.CUDAGraph()
+        keep = sp
+        try:
+            with torch.cuda.graph(g):
+                sp = torch.cuda.current_stream().cuda_stream   # the launches read sp when called
+                for i in range(n):
+                    rc = fns[i % R]()
+                    if rc != 0:
+                        raise _lib.ApmoeError(rc, name)
+        finally:
+            sp = keep
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / (reps * n)
+
+    graph_us = {}
+    if use_graph:
+        for name in names:
+            if name.endswith(("_gemv", "_tile")):
+                graph_us[name] = launch_graph_us(name)
+    dom_us_eager = dom_us
+    dom_us = graph_us.get(dominant, dom_us)
     layer_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     dom_bytes = by.get(dominant, 0)
     if dominant.endswith("_tile"):
@@ -571,12 +609,12 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": dom_flops / (dom_us * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
                     "traffic": counted_traffic(dominant, cfg.name), "algorithmic_flops": dom_flops,
-                    "algorithmic_bytes": dom_bytes, "avg_us": dom_us}
+                    "algorithmic_bytes": dom_bytes, "avg_us": dom_us, "avg_us_eager": dom_us_eager}
     else:
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": counted_traffic(dominant, cfg.name),
-                    "algorithmic_bytes": dom_bytes, "avg_us": dom_us}
+                    "algorithmic_bytes": dom_bytes, "avg_us": dom_us, "avg_us_eager": dom_us_eager}
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -602,11 +640,13 @@ def measure(args, cfg, inp, bits, steps, warmup, probe_steps, time_stats=True):
         "expert_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "roofline": roofline,
         "per_launch_us": {n: round(per[n], 2) for n in names},
+        "launch_us_graph": {n: round(v, 2) for n, v in graph_us.items()},
         "route_stats_us": None if route_stats_us is None else round(route_stats_us, 2),
         "route_stats_in_step_us": None if route_stats_in_step_us is None else round(route_stats_in_step_us, 2),
         "per_launch_bytes": {n: int(by.get(n, 0)) for n in names},
     }
-    gu, dn = per.get("gate_up_gemv"), per.get("down_gemv")
+    gu = graph_us.get("gate_up_gemv", per.get("gate_up_gemv"))
+    dn = graph_us.get("down_gemv", per.get("down_gemv"))
     if gu and dn and by["gate_up_gemv"] + by["down_gemv"] > 0:   # the two GEMV stages together against HBM peak
         gb = (by["gate_up_gemv"] + by["down_gemv"]) / ((gu + dn) * 1e-6) / 1e9
         result["gemv_stages"] = {"algorithmic_bytes": int(by["gate_up_gemv"] + by["down_gemv"]),
